@@ -1,0 +1,165 @@
+"""ctypes binding of libfa2.so -- argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module
+turns torch tensors into device pointers and sizes, picks the current torch
+stream, and turns status codes into exceptions.  There is no fallback: if the
+library is missing the call fails loudly.
+
+Names mirror include/fa2.h: fa2_fwd, fa2_bwd, fa2_bwd_workspace_bytes,
+fa2_status_string.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfa2.so")
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+class Fa2Error(RuntimeError):
+    """A nonzero fa2_status returned by the library."""
+
+    def __init__(self, status: int):
+        self.status = int(status)
+        super().__init__(fa2_status_string(self.status))
+
+
+def lib():
+    """Load libfa2.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- loads the HIP runtime first
+
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m exact_tiled_attention_30_amd.build` "
+            "(hipcc --offload-arch=gfx950) first")
+    L = ctypes.CDLL(LIB_PATH)
+    L.fa2_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _vp]
+    L.fa2_fwd.restype = _i
+    L.fa2_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+    L.fa2_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.fa2_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                          _i, _i, _i, _i, _i, ctypes.c_float, _vp]
+    L.fa2_bwd.restype = _i
+    L.fa2_status_string.argtypes = [_i]
+    L.fa2_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def fa2_status_string(status: int) -> str:
+    return lib().fa2_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise Fa2Error(status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    import torch
+
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _bnhd(q):
+    if q.dim() != 4:
+        raise ValueError("expected a [B, N, H, d] tensor")
+    B, N, H, d = (int(x) for x in q.shape)
+    return B, N, H, d
+
+
+def _require(t, dtype, name):
+    import torch
+
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    del torch
+
+
+def fa2_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """Enqueue the forward pass on `stream` (default: torch's current stream).
+
+    q, k, v, o: bf16 [B, N, H, d]; lse: fp32 [B, H, N].  Raises Fa2Error."""
+    import torch
+
+    B, N, H, d = _bnhd(q)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _require(t, torch.bfloat16, name)
+        if tuple(t.shape) != (B, N, H, d):
+            raise ValueError(f"{name} must have shape {(B, N, H, d)}")
+    _require(lse, torch.float32, "lse")
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"lse must have shape {(B, H, N)}")
+    _check(lib().fa2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                         int(bool(causal)), float(scale), _stream(q, stream)))
+
+
+def fa2_bwd_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    return int(lib().fa2_bwd_workspace_bytes(B, H, N, d, int(bool(causal))))
+
+
+def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool, scale: float,
+            stream=None) -> None:
+    """Enqueue the backward pass. workspace: a uint8 device tensor of at least
+    fa2_bwd_workspace_bytes(...) bytes.  Raises Fa2Error."""
+    import torch
+
+    B, N, H, d = _bnhd(q)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"),
+                    (dk, "dk"), (dv, "dv")):
+        _require(t, torch.bfloat16, name)
+        if tuple(t.shape) != (B, N, H, d):
+            raise ValueError(f"{name} must have shape {(B, N, H, d)}")
+    _require(lse, torch.float32, "lse")
+    _require(workspace, torch.uint8, "workspace")
+    _check(lib().fa2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, H, N, d,
+                         int(bool(causal)), float(scale), _stream(q, stream)))
+
+
+# ---- conveniences that allocate the outputs with torch, then call the above
+
+def attention_forward(q, k, v, causal: bool = False, scale: float | None = None):
+    """Allocate O and L, run fa2_fwd, return (o, lse)."""
+    import torch
+
+    B, N, H, d = _bnhd(q)
+    if scale is None:
+        scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa2_fwd(q, k, v, o, lse, causal, scale)
+    return o, lse
+
+
+def attention_backward(q, k, v, o, lse, dout, causal: bool = False,
+                       scale: float | None = None):
+    """Allocate dQ, dK, dV and the workspace, run fa2_bwd, return (dq, dk, dv)."""
+    import torch
+
+    B, N, H, d = _bnhd(q)
+    if scale is None:
+        scale = d ** -0.5
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(1, fa2_bwd_workspace_bytes(B, H, N, d, causal)), dtype=torch.uint8,
+                     device=q.device)
+    fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, causal, scale)
+    return dq, dk, dv

@@ -1,0 +1,136 @@
+// fa2_api.cpp -- the C ABI of libfa2.so (declared in include/fa2.h).
+//
+// Every argument is checked on the host before any HIP runtime call, so each
+// error path is reachable without a GPU; only then is the kernel for the
+// requested (d, causal) enqueued on the caller's stream.
+#include "fa2.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa2_internal.hpp"
+
+namespace {
+
+constexpr size_t kMaxElems = (size_t)1 << 62;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = (uintptr_t)p;
+  return Range{a, a + bytes};
+}
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+// Shape checks shared by both passes.  *elems receives B*N*H*d.
+int check_shape(int B, int H, int N, int d, float scale, size_t* elems, size_t* rows) {
+  if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
+  if (!isfinite(scale)) return FA2_ERR_SCALE;
+  const long double e = (long double)B * H * N * d;
+  if (e > (long double)kMaxElems) return FA2_ERR_SHAPE;
+  // grid = B * H * ceil(N / 128) workgroups must fit the launch limit
+  const long double grid = (long double)B * H * ((N + 127) / 128);
+  if (grid > 2147483647.0L) return FA2_ERR_SHAPE;
+  *elems = (size_t)B * H * N * d;
+  *rows = (size_t)B * H * N;
+  return FA2_OK;
+}
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace fa2 {
+size_t bwd_delta_bytes(int B, int H, int N) { return align256((size_t)B * H * N * sizeof(float)); }
+size_t bwd_dq_acc_bytes(int B, int H, int N, int d) {
+  return align256((size_t)B * H * N * d * sizeof(float));
+}
+}  // namespace fa2
+
+extern "C" {
+
+const char* fa2_status_string(int status) {
+  switch (status) {
+    case FA2_OK: return "FA2_OK";
+    case FA2_ERR_NULLPTR: return "FA2_ERR_NULLPTR: a required pointer is NULL";
+    case FA2_ERR_SHAPE: return "FA2_ERR_SHAPE: negative or too large B, H or N";
+    case FA2_ERR_HEADDIM: return "FA2_ERR_HEADDIM: head dimension must be 64 or 128";
+    case FA2_ERR_SCALE: return "FA2_ERR_SCALE: scale must be finite";
+    case FA2_ERR_ALIGN: return "FA2_ERR_ALIGN: tensor base pointer misaligned";
+    case FA2_ERR_ALIAS: return "FA2_ERR_ALIAS: an output overlaps another tensor";
+    case FA2_ERR_WORKSPACE: return "FA2_ERR_WORKSPACE: workspace missing or too small";
+    case FA2_ERR_LAUNCH: return "FA2_ERR_LAUNCH: the HIP runtime rejected a launch";
+    default: return "unknown fa2 status";
+  }
+}
+
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+            int N, int d, int causal, float scale, void* stream) {
+  size_t elems = 0, rows = 0;
+  const int st = check_shape(B, H, N, d, scale, &elems, &rows);
+  if (st != FA2_OK) return st;
+  if (elems == 0) return FA2_OK;
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_NULLPTR;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return FA2_ERR_ALIGN;
+  const size_t tb = elems * 2, lb = rows * sizeof(float);
+  const Range rq = range_of(q, tb), rk = range_of(k, tb), rv = range_of(v, tb);
+  const Range ro = range_of(o, tb), rl = range_of(lse, lb);
+  for (const Range& out : {ro, rl})
+    for (const Range& in : {rq, rk, rv})
+      if (overlap(out, in)) return FA2_ERR_ALIAS;
+  if (overlap(ro, rl)) return FA2_ERR_ALIAS;
+
+  fa2::FwdParams p{q, k, v, o, lse, B, H, N, d, causal != 0, scale, (hipStream_t)stream};
+  return fa2::launch_fwd(p) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d, int causal) {
+  (void)causal;
+  size_t elems = 0, rows = 0;
+  if (check_shape(B, H, N, d, 1.0f, &elems, &rows) != FA2_OK || elems == 0) return 0;
+  return fa2::bwd_delta_bytes(B, H, N) + fa2::bwd_dq_acc_bytes(B, H, N, d);
+}
+
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, void* workspace,
+            size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
+            void* stream) {
+  size_t elems = 0, rows = 0;
+  const int st = check_shape(B, H, N, d, scale, &elems, &rows);
+  if (st != FA2_OK) return st;
+  if (elems == 0) return FA2_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA2_ERR_NULLPTR;
+  if (!workspace || workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d, causal))
+    return FA2_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 16))
+    return FA2_ERR_ALIGN;
+  const size_t tb = elems * 2, lb = rows * sizeof(float);
+  const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb),
+                       range_of(lse, lb), range_of(dout, tb)};
+  const Range outs[] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
+                        range_of(workspace, workspace_bytes)};
+  for (const Range& out : outs)
+    for (const Range& in : ins)
+      if (overlap(out, in)) return FA2_ERR_ALIAS;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return FA2_ERR_ALIAS;
+
+  char* ws = (char*)workspace;
+  fa2::BwdParams p{q, k, v, o, lse, dout, dq, dk, dv,
+                   (float*)ws, (float*)(ws + fa2::bwd_delta_bytes(B, H, N)),
+                   B, H, N, d, causal != 0, scale, (hipStream_t)stream};
+  return fa2::launch_bwd(p) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,306 @@
+// fa2_fwd.hip -- FlashAttention-2 forward pass for gfx950.
+//
+// Algorithm: infra-guide page "6.2 FlashAttention V2 in depth", section 6.1
+// (Q-tile outer loop, K/V-tile inner loop, running max m and sum l, one
+// division by l after the loop, logsumexp saved for the backward), with the
+// causal block skipping of section 5.3 and the split-Q warp partition of
+// section 4.2.  Design for CDNA4, not a port of the A100 kernel:
+//
+//  * One workgroup = one 128-row Q tile of one (batch, head); 4 waves of 64
+//    lanes, each wave owns 32 query rows and its softmax rows outright (no
+//    cross-wave merge).  Grid = B * H * ceil(N / 128), renumbered so each XCD
+//    runs contiguous Q tiles of the same heads (shared K/V in its L2); causal
+//    grids run the heaviest (last) Q tiles of a head first.
+//  * Both products run on v_mfma_f32_32x32x16_bf16 in transposed form:
+//    S^T = K Q^T (A = K rows from LDS, B = Q held in VGPRs for the whole
+//    loop) and O^T = V^T P^T (A = V^T from LDS, B = P^T straight from the
+//    S^T accumulators after an in-register bf16 conversion).  In both, the
+//    accumulator column -- one query -- is fixed per lane, so row max, row sum,
+//    rescale and the final 1/l are per-lane scalars plus one exchange between
+//    the two lane halves.
+//  * K/V tiles are double-buffered in LDS: the next tile's global loads are
+//    issued (128-bit, coalesced) before the current tile's math and written to
+//    the other buffer afterwards; one barrier per tile.  V is transposed on the
+//    way into LDS so the PV operand reads are contiguous 64-bit loads.
+//  * Softmax in base 2: t = s * scale*log2(e) in fp32 on the MFMA output
+//    (never folded into bf16 Q), P = exp2(t - m).  l is summed from the fp32
+//    P before the bf16 conversion.  The reference max m is only moved when a
+//    row's tile max exceeds it by more than kRescaleSlack (log2 units), so the
+//    O rescale (a multiply of every accumulator) is skipped on most tiles; the
+//    stored O/l and L = ln2 * (m + log2 l) are mathematically unchanged, and
+//    P stays <= 2^kRescaleSlack, far from fp32/bf16 overflow.
+//  * Causal: K/V tiles past the Q tile's last row are never visited; a wave
+//    skips tiles entirely above its rows; only tiles crossing the diagonal (or
+//    the ragged end of the sequence) run the element mask.
+#include <math.h>
+
+#include "fa2_device.hpp"
+#include "fa2_internal.hpp"
+
+namespace fa2 {
+namespace {
+
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int BC>
+struct FwdCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kRowsPerWave = 32;
+  static constexpr int BR = kWaves * kRowsPerWave;
+  // LDS row strides (bf16 elements).  K rows are padded by 16 bytes so 8
+  // lanes reading 16 bytes each from 8 consecutive rows hit distinct banks;
+  // V^T rows by 8 bytes so 16 lanes reading 8 bytes from 16 rows do.
+  static constexpr int kKStride = D + 8;
+  static constexpr int kVStride = BC + 4;
+  static constexpr int kKTile = BC * kKStride;
+  static constexpr int kVTile = D * kVStride;
+  // Global -> LDS staging work per thread.
+  static constexpr int kKChunks = BC * D / 8 / kThreads;  // 16-byte K chunks
+  static constexpr int kKeysPerUnit = ((BC / 4) * (D / 8)) % kThreads == 0 ? 4 : 2;
+  static constexpr int kVUnits = (BC / kKeysPerUnit) * (D / 8) / kThreads;
+  static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
+  static_assert(kKChunks * kThreads * 8 == BC * D, "K staging must cover the tile");
+  static_assert(kVUnits * kThreads * kKeysPerUnit * 8 == BC * D, "V staging must cover the tile");
+};
+
+// Two bf16 from element i of two 8-element rows, packed (row a in the low half).
+__device__ __forceinline__ uint32_t pack_col(const u32x4& a, const u32x4& b, int i) {
+  const uint32_t x = a[i / 2], y = b[i / 2];
+  return (i & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+}
+
+template <int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
+    int H, int N, int n_qtiles, int grid, float c, uint32_t q_sign) {
+  using C = FwdCfg<D, BC>;
+  constexpr int KPU = C::kKeysPerUnit;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2 * C::kKTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2 * C::kVTile];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane % 32, hi = lane / 32;
+
+  // ---- tile scheduler: workgroup -> (batch, head, Q tile)
+  const int logical = xcd_contiguous_id(blockIdx.x, grid);
+  const int bh = logical / n_qtiles;
+  int qt = logical % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest Q tiles of a head first
+  const int b = bh / H, hh = bh % H;
+  const int q0 = qt * C::BR;
+  const int qw0 = q0 + wave * C::kRowsPerWave;  // first query row of this wave
+  const int my_q = qw0 + l32;                   // the query row this lane owns
+  const size_t tok = (size_t)H * D;             // elements between tokens
+  const size_t head = (size_t)b * N * tok + (size_t)hh * D;
+
+  // ---- Q tile -> B-operand fragments, kept in VGPRs for the whole loop.
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qp = q + head + (size_t)my_q * tok + 8 * hi;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (my_q < N) x = *(const u32x4*)(qp + 16 * cc);
+      x ^= q_sign;  // negative scale: negate Q (exact), use |scale|
+      qf[cc] = as_bf16x8(x);
+    }
+  }
+
+  const int kv_len = CAUSAL ? min(N, q0 + C::BR) : N;
+  const int n_kv = (kv_len + BC - 1) / BC;
+
+  // ---- K/V staging through registers into the double-buffered LDS tiles.
+  u32x4 kreg[C::kKChunks];
+  u32x4 vreg[C::kVUnits][KPU];
+  auto load_tile = [&](int jt) {
+    const int kv0 = jt * BC;
+#pragma unroll
+    for (int it = 0; it < C::kKChunks; ++it) {
+      const int ci = tid + it * C::kThreads;
+      const int key = ci / (D / 8), dc = ci % (D / 8);
+      const int gk = kv0 + key;
+      kreg[it] = u32x4{0u, 0u, 0u, 0u};
+      if (gk < N) kreg[it] = *(const u32x4*)(k + head + (size_t)gk * tok + dc * 8);
+    }
+#pragma unroll
+    for (int it = 0; it < C::kVUnits; ++it) {
+      const int ui = tid + it * C::kThreads;
+      const int kg = ui / (D / 8), dc = ui % (D / 8);
+#pragma unroll
+      for (int kk = 0; kk < KPU; ++kk) {
+        const int gk = kv0 + kg * KPU + kk;
+        vreg[it][kk] = u32x4{0u, 0u, 0u, 0u};
+        if (gk < N) vreg[it][kk] = *(const u32x4*)(v + head + (size_t)gk * tok + dc * 8);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* kd = ks + buf * C::kKTile;
+#pragma unroll
+    for (int it = 0; it < C::kKChunks; ++it) {
+      const int ci = tid + it * C::kThreads;
+      const int key = ci / (D / 8), dc = ci % (D / 8);
+      *(u32x4*)(kd + key * C::kKStride + dc * 8) = kreg[it];
+    }
+    uint16_t* vd = vt + buf * C::kVTile;
+#pragma unroll
+    for (int it = 0; it < C::kVUnits; ++it) {
+      const int ui = tid + it * C::kThreads;
+      const int kg = ui / (D / 8), dc = ui % (D / 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint16_t* dst = vd + (dc * 8 + i) * C::kVStride + kg * KPU;
+        if constexpr (KPU == 4) {
+          *(u32x2*)dst = u32x2{pack_col(vreg[it][0], vreg[it][1], i),
+                               pack_col(vreg[it][2], vreg[it][3], i)};
+        } else {
+          *(uint32_t*)dst = pack_col(vreg[it][0], vreg[it][1], i);
+        }
+      }
+    }
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY;  // reference max of this row, log2 units
+  float l_part = 0.f;       // this lane's share of the row sum, relative to m_run
+
+  if (n_kv > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int jt = 0; jt < n_kv; ++jt) {
+    const int buf = jt & 1;
+    if (jt + 1 < n_kv) load_tile(jt + 1);
+    const int kv0 = jt * BC;
+    const bool wave_active = !CAUSAL || kv0 <= qw0 + C::kRowsPerWave - 1;
+    if (wave_active) {
+      const uint16_t* kb = ks + buf * C::kKTile;
+      const uint16_t* vb = vt + buf * C::kVTile;
+
+      // S^T = K_j Q_i^T (scores of this lane's query against BC keys)
+      f32x16 s[BC / 32];
+#pragma unroll
+      for (int kt = 0; kt < BC / 32; ++kt) s[kt] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) {
+#pragma unroll
+        for (int kt = 0; kt < BC / 32; ++kt) {
+          const bf16x8 a = *(const bf16x8*)(kb + (kt * 32 + l32) * C::kKStride + cc * 16 + hi * 8);
+          s[kt] = mfma32(a, qf[cc], s[kt]);
+        }
+      }
+
+      // element mask on diagonal-crossing and ragged tiles only
+      const bool need_mask = (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N);
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < BC / 32; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kt * 32 + acc_row(r, hi);
+            const bool visible = key < N && (!CAUSAL || key <= my_q);
+            if (!visible) s[kt][r] = -INFINITY;
+          }
+      }
+
+      // online softmax statistics
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < BC / 32; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+      if (wave_any(mt > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+        l_part *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < BC / 32; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(s[kt][r], c, -mref));
+          if (need_mask && s[kt][r] == -INFINITY) p = 0.f;
+          s[kt][r] = p;
+          rs += p;
+        }
+      l_part += rs;
+
+      // O^T += V_j^T P^T: the P^T operand is the S^T accumulator, converted.
+      // Contraction slot t of lane half hi pairs with key
+      // 16*cc + 8*(t/4) + 4*hi + t%4 in both operands.
+#pragma unroll
+      for (int cc = 0; cc < BC / 16; ++cc) {
+        const f32x16& sv = s[cc / 2];
+        const int r0 = 8 * (cc % 2);
+        const bf16x8 pf = to_bf16x8(f32x8{sv[r0 + 0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3],
+                                          sv[r0 + 4], sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]});
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const uint16_t* vr = vb + (dt * 32 + l32) * C::kVStride + cc * 16 + 4 * hi;
+          const u32x2 lo = *(const u32x2*)vr;
+          const u32x2 up = *(const u32x2*)(vr + 8);
+          oacc[dt] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], up[0], up[1]}), pf, oacc[dt]);
+        }
+      }
+    }
+    if (jt + 1 < n_kv) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: one division by l per row, bf16 O, natural-log L
+  const float l = l_part + swap_halves(l_part);
+  const float inv = 1.0f / l;
+  if (my_q < N) {
+    uint16_t* op = o + head + (size_t)my_q * tok;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = f32x4{oacc[dt][4 * g + 0], oacc[dt][4 * g + 1], oacc[dt][4 * g + 2],
+                              oacc[dt][4 * g + 3]} * inv;
+        *(u32x2*)(op + dt * 32 + 8 * g + 4 * hi) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+      }
+    if (hi == 0) lse[((size_t)b * H + hh) * N + my_q] = (m_run + log2f(l)) * kLn2;
+  }
+}
+
+template <int D, int BC, bool CAUSAL>
+hipError_t launch_fwd_t(const FwdParams& p) {
+  using C = FwdCfg<D, BC>;
+  const int n_qtiles = (p.N + C::BR - 1) / C::BR;
+  const long long grid = (long long)p.B * p.H * n_qtiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const float c = (float)(fabs((double)p.scale) * 1.4426950408889634);
+  const uint32_t q_sign = p.scale < 0.f ? 0x80008000u : 0u;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((fwd_kernel<D, BC, CAUSAL>), dim3((unsigned)grid), dim3(C::kThreads), 0,
+                     p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
+                     (uint16_t*)p.o, p.lse, p.H, p.N, n_qtiles, (int)grid, c, q_sign);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdParams& p) {
+  if (p.d == 64) {
+    return p.causal ? launch_fwd_t<64, 64, true>(p) : launch_fwd_t<64, 64, false>(p);
+  }
+  return p.causal ? launch_fwd_t<128, 64, true>(p) : launch_fwd_t<128, 64, false>(p);
+}
+
+}  // namespace fa2

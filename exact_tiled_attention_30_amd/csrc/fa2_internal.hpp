@@ -1,0 +1,47 @@
+// fa2_internal.hpp -- host-side interface between the C ABI layer and the
+// kernel translation units.  Not installed; callers use include/fa2.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa2 {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  bool causal;
+  float scale;
+  hipStream_t stream;
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;   // D vector, fp32 [B, H, N] (workspace)
+  float* dq_acc;  // fp32 [B, N, H, d] (workspace)
+  int B, H, N, d;
+  bool causal;
+  float scale;
+  hipStream_t stream;
+};
+
+// Workspace layout of the backward pass (offsets in bytes, 256-aligned).
+size_t bwd_delta_bytes(int B, int H, int N);
+size_t bwd_dq_acc_bytes(int B, int H, int N, int d);
+
+hipError_t launch_fwd(const FwdParams& p);
+hipError_t launch_bwd(const BwdParams& p);
+
+}  // namespace fa2

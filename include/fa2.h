@@ -1,0 +1,107 @@
+/*
+ * fa2.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library, libfa2.so.
+ *
+ * Exact attention, computed tile by tile without forming the N x N score
+ * matrix:
+ *
+ *     O  = softmax(scale * Q K^T + M) V,     L = rowwise logsumexp of the same
+ *                                                scaled, masked scores
+ *
+ * with M = 0 (non-causal) or M_ij = -inf for j > i (causal).  The problem
+ * statement, the saved logsumexp and the causal mask follow the infra-guide
+ * page "6.2 FlashAttention V2 in depth": section 6.1 (forward algorithm and
+ * its outputs O and L), section 5.1 (the mask keeps the lower triangle,
+ * diagonal included) and section 7 (backward inputs Q, K, V, O, L, dO;
+ * outputs dQ, dK, dV; the D vector of section 7.3).  The abstract of
+ * "FlashAttention-2: Faster Attention with Better Parallelism and Work
+ * Partitioning" fixes that the result is exact, not an approximation.
+ *
+ * Common conventions
+ *  - Self-attention: queries and keys share one sequence length N.
+ *  - Q, K, V, O, dO, dQ, dK, dV: bfloat16, [B, N, H, d] contiguous row-major
+ *    (element (b, n, h, c) at ((b*N + n)*H + h)*d + c).
+ *  - L (lse): float32, [B, H, N] contiguous; natural-log logsumexp of the
+ *    scaled, masked scores of each query row.
+ *  - d must be 64 or 128.  B, H, N >= 0; B*H*N == 0 is a successful no-op.
+ *  - scale: any finite float (usually 1/sqrt(d)).
+ *  - Every pointer is a DEVICE pointer owned by the caller; the library keeps
+ *    no reference after the call returns and allocates no device memory.
+ *    Tensor base pointers must be 16-byte aligned (lse 4-byte aligned).
+ *    Outputs must not overlap inputs or each other.
+ *  - stream is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously; device-side faults surface at the caller's next
+ *    synchronisation.
+ *  - Argument checking happens on the host before any HIP call; on error
+ *    nothing is enqueued and a nonzero fa2_status is returned.
+ *  - No global mutable state: concurrent calls on different streams are safe.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa2_status {
+  FA2_OK = 0,
+  FA2_ERR_NULLPTR = 1,   /* a required pointer is NULL and the problem is non-empty */
+  FA2_ERR_SHAPE = 2,     /* B, H or N negative, or the tensor size overflows      */
+  FA2_ERR_HEADDIM = 3,   /* d is not 64 or 128                                    */
+  FA2_ERR_SCALE = 4,     /* scale is NaN or infinite                              */
+  FA2_ERR_ALIGN = 5,     /* a base pointer is not 16-byte (lse: 4-byte) aligned   */
+  FA2_ERR_ALIAS = 6,     /* an output range overlaps an input or another output   */
+  FA2_ERR_WORKSPACE = 7, /* backward workspace missing or smaller than required   */
+  FA2_ERR_LAUNCH = 8     /* the HIP runtime rejected a kernel launch              */
+} fa2_status;
+
+/*
+ * Forward pass ("6.2 FlashAttention V2 in depth", section 6.1; causal block
+ * skipping of section 5.3).
+ *   q, k, v : inputs, bf16 [B, N, H, d]
+ *   o       : output, bf16 [B, N, H, d]; O = softmax(scale*QK^T + M) V,
+ *             rounded to nearest even
+ *   lse     : output, fp32 [B, H, N]; L_i = log sum_j exp(scale*q_i.k_j + M_ij)
+ *   causal  : nonzero applies the lower-triangular mask (key j visible to
+ *             query i iff j <= i)
+ * Returns FA2_OK or an fa2_status error code.
+ */
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * Bytes of device workspace fa2_bwd needs for these sizes (0 if the problem
+ * is empty or the arguments are invalid).  Holds the D vector (fp32 [B,H,N])
+ * and an fp32 dQ accumulator ([B, N, H, d]).
+ */
+size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d, int causal);
+
+/*
+ * Backward pass ("6.2 FlashAttention V2 in depth", section 7: P is recovered
+ * from the saved logsumexp, dK and dV are owned by the block that holds a
+ * key/value tile, dQ is summed across blocks, and D_i = rowsum(dO_i * O_i) is
+ * computed once by a separate pre-processing kernel).
+ *   q, k, v : forward inputs, bf16 [B, N, H, d]
+ *   o, lse  : forward outputs of fa2_fwd for the same q, k, v, causal, scale
+ *   dout    : gradient of the loss w.r.t. o, bf16 [B, N, H, d]
+ *   dq, dk, dv : outputs, bf16 [B, N, H, d]
+ *   workspace  : device scratch of at least fa2_bwd_workspace_bytes() bytes,
+ *                16-byte aligned; its contents on entry are ignored and are
+ *                overwritten.  Calls that share one workspace must be ordered
+ *                on one stream.
+ * Returns FA2_OK or an fa2_status error code.
+ */
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o,
+            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+            int causal, float scale, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa2_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

@@ -1,0 +1,135 @@
+"""GPU parity of the forward pass against the fp64 oracle.
+
+Small shapes (several tiles, ragged tails, edge sizes) are compared element by
+element in full; every full-size forward workload is run in the launch
+configuration the benchmark times and compared on sampled rows, which the
+oracle computes one by one (rows are independent).  Tolerances: see
+oracle/compare.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_tiled_attention_30_amd import binding
+from exact_tiled_attention_30_amd.inputs import WORKLOADS, make_inputs
+from oracle.compare import forward_report
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(x):
+    return {n: t.cuda() for n, t in x.items()}
+
+
+def run_fwd(x, causal, scale):
+    d = _dev(x)
+    o, lse = binding.attention_forward(d["q"], d["k"], d["v"], causal, scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+SMALL_SHAPES = [
+    # (B, H, N, d)
+    (1, 1, 128, 64),     # one Q tile, two K/V tiles
+    (1, 1, 1, 64),       # a single token
+    (1, 1, 1, 128),
+    (2, 3, 200, 64),     # ragged Q and K/V tails
+    (1, 2, 333, 128),
+    (2, 1, 64, 128),     # one K/V tile, half a Q tile
+    (1, 2, 257, 128),    # one row past a tile edge
+    (1, 1, 1000, 64),
+    (3, 2, 129, 64),
+    (1, 1, 520, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "b{}h{}n{}d{}".format(*s))
+def test_small_shapes_every_element(shape, causal):
+    B, H, N, d = shape
+    x = make_inputs(B, H, N, d, seed=11)
+    scale = d ** -0.5
+    print(f"[fwd small] shape={shape} causal={causal}", flush=True)
+    o, lse = run_fwd(x, causal, scale)
+    o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal, scale)
+    rep = forward_report(o, lse, o_ref, lse_ref)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1.0 / 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_unusual_scales(scale, causal):
+    B, H, N, d = 1, 2, 300, 64
+    x = make_inputs(B, H, N, d, seed=5, peaked_fraction=0.02)
+    print(f"[fwd scale] scale={scale} causal={causal}", flush=True)
+    o, lse = run_fwd(x, causal, scale)
+    o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal, scale)
+    rep = forward_report(o, lse, o_ref, lse_ref)
+    assert rep["ok"], rep
+
+
+def test_empty_problem_is_a_noop():
+    q = torch.empty((2, 0, 3, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = binding.attention_forward(q, q, q, True, 0.125)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and lse.numel() == 0
+
+
+def test_side_stream_and_determinism():
+    B, H, N, d = 2, 4, 700, 128
+    x = _dev(make_inputs(B, H, N, d, seed=3))
+    s = torch.cuda.Stream()
+    outs = []
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            o, lse = binding.attention_forward(x["q"], x["k"], x["v"], True, d ** -0.5)
+            outs.append((o, lse))
+    s.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+    o_ref, lse_ref = oracle.attention_forward(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(),
+                                              True, d ** -0.5)
+    rep = forward_report(outs[0][0].cpu(), outs[0][1].cpu(), o_ref, lse_ref)
+    assert rep["ok"], rep
+
+
+def sample_rows(B, H, N, n_random=48, seed=0):
+    rng = np.random.default_rng(seed)
+    edge = {0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, N // 2,
+            N - 129, N - 128, N - 65, N - 64, N - 2, N - 1}
+    idx = sorted(i for i in edge if 0 <= i < N)
+    heads = {(0, 0), (B - 1, H - 1)}
+    while len(heads) < min(4, B * H):
+        heads.add((int(rng.integers(B)), int(rng.integers(H))))
+    rows = []
+    for (b, h) in sorted(heads):
+        for i in idx:
+            rows.append((b, h, i))
+    for _ in range(n_random):
+        rows.append((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(N))))
+    return np.array(rows, dtype=np.int64)
+
+
+FWD_WORKLOADS = [w for w in WORKLOADS.values() if not w.backward]
+
+
+@pytest.mark.parametrize("w", FWD_WORKLOADS, ids=lambda w: w.name)
+def test_full_size_workloads_sampled_rows(w):
+    print(f"[fwd full-size] {w.name}", flush=True)
+    x = make_inputs(w.B, w.H, w.N, w.d, seed=w.seed, peaked_fraction=w.peaked_fraction)
+    d = _dev(x)
+    o = torch.empty_like(d["q"])
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    binding.fa2_fwd(d["q"], d["k"], d["v"], o, lse, w.causal, w.scale)
+    torch.cuda.synchronize()
+    del d
+    rows = sample_rows(w.B, w.H, w.N)
+    o_ref, lse_ref = oracle.attention_forward_rows(x["q"], x["k"], x["v"], w.causal, w.scale,
+                                                   rows)
+    b, h, i = (torch.as_tensor(rows[:, c], device="cuda") for c in range(3))
+    o_got = o[b, i, h].cpu()
+    lse_got = lse[b, h, i].cpu()
+    rep = forward_report(o_got, lse_got, o_ref, lse_ref)
+    print(f"  {rep}", flush=True)
+    assert rep["ok"], rep
