@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Throughput of the FlashAttention-2 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+One step is one pass of the hot path over one batch of resident, seeded
+synthetic inputs.  The default workload is B=8, H=16, N=1024, d=64 run both
+ways: a step is the non-causal forward followed by the causal forward on the
+same Q, K, V.  Other workloads (exact_tiled_attention_30_amd.inputs.WORKLOADS)
+can be named with --workload; a backward workload's step is one fa2_bwd call
+on O and L produced by fa2_fwd beforehand.
+
+FLOPs follow the usual convention: 4*B*H*N^2*d per forward, halved if causal;
+a backward pass counts 2.5x its forward.  Timing uses HIP events on the stream
+the kernels are launched on, with an event pair around every launch, so each
+kernel's average duration is measured inside the timed region as well.
+
+Prints ONE JSON line.  Besides the throughput it carries:
+  roofline      the dominant kernel's achieved TFLOP/s against the bf16 dense
+                MFMA peak, and its HBM traffic from the committed rocprofv3
+                counter summary (null when the kernel source changed since);
+  cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample of
+                rows of the same workload, scaled to TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd attention TFLOP/s (4BHN²d, ½ if causal) and % of MI355X bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz (dense)
+DEFAULT_PAIR = ("fwd_b8_h16_n1024_d64_full", "fwd_b8_h16_n1024_d64_causal")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_digest() -> str:
+    """Digest of the kernel sources; counter figures are tied to it."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_tiled_attention_30_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str):
+    """HBM bytes per launch measured by rocprofv3 for this kernel, if current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(kernel_key)
+    if not entry or entry.get("source_digest") != kernel_source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=None,
+                   help="one workload name (default: the N=1024 d=64 pair)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_30_amd import binding
+    from exact_tiled_attention_30_amd.inputs import WORKLOADS, inputs_for
+
+    names = DEFAULT_PAIR if args.workload is None else (args.workload,)
+    ws = [WORKLOADS[n] for n in names]
+    base = ws[0]
+    for w in ws[1:]:
+        assert (w.B, w.H, w.N, w.d) == (base.B, base.H, base.N, base.d)
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    host = inputs_for(base)
+    x = {n: t.to(dev) for n, t in host.items()}
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((base.B, base.H, base.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    launches = []  # (label, callable, flops)
+    for w in ws:
+        if not w.backward:
+            def fwd(w=w):
+                binding.fa2_fwd(x["q"], x["k"], x["v"], o, lse, w.causal, w.scale)
+            launches.append((w.name, fwd, w.flops()))
+        else:
+            binding.fa2_fwd(x["q"], x["k"], x["v"], o, lse, w.causal, w.scale)
+            dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
+            wsp = torch.empty(binding.fa2_bwd_workspace_bytes(w.B, w.H, w.N, w.d, w.causal),
+                              dtype=torch.uint8, device=dev)
+
+            def bwd(w=w, dq=dq, dk=dk, dv=dv, wsp=wsp):
+                binding.fa2_bwd(x["q"], x["k"], x["v"], o, lse, x["dout"], dq, dk, dv, wsp,
+                                w.causal, w.scale)
+            launches.append((w.name, bwd, w.flops()))
+
+    for _ in range(args.warmup):
+        for _, fn, _ in launches:
+            fn()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+          for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(K):
+        ev[s][0].record(stream)
+        for j, (_, fn, _) in enumerate(launches):
+            fn()
+            ev[s][j + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    step_flops = sum(f for _, _, f in launches)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    per_kernel_ms = [float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)]))
+                     for j in range(len(launches))]
+    dom = int(np.argmax(per_kernel_ms))
+    dom_name, _, dom_flops = launches[dom]
+    achieved = dom_flops / (per_kernel_ms[dom] * 1e-3) / 1e12
+
+    roofline = {
+        "bound": "mfma",
+        "kernel": dom_name,
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": load_traffic(dom_name),
+        "avg_launch_ms": round(per_kernel_ms[dom], 5),
+        "flops_per_launch": dom_flops,
+    }
+
+    cpu = None if args.no_cpu else cpu_baseline(ws, host, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "+".join(w.name for w in ws),
+            "B": base.B, "H": base.H, "N": base.N, "d": base.d,
+            "causal": [w.causal for w in ws],
+            "backward": [w.backward for w in ws],
+            "layout": "[B,N,H,d] bf16 in/out, fp32 lse [B,H,N]",
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "per_kernel": {n: {"ms": round(t, 5),
+                           "tflops": round(f / (t * 1e-3) / 1e12, 2)}
+                       for (n, _, f), t in zip(launches, per_kernel_ms)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(ws, host, target_s):
+    """Time the fp64 oracle on a bounded sample of rows of the same workload.
+
+    Rows are independent, so the FLOPs of a sample are exact: 4*n_vis*d per
+    row (n_vis visible keys).  Inputs are widened to fp64 once, outside the
+    timed calls; the sample size comes from a short calibration run.
+    """
+    import numpy as np
+
+    import oracle
+
+    if any(w.backward for w in ws):
+        return None
+    n_thr = oracle.num_threads()
+    rng = np.random.default_rng(0)
+    q64, k64, v64 = (oracle.widen(host[n]) for n in ("q", "k", "v"))
+
+    def rows_for(w, n):
+        return np.stack([rng.integers(w.B, size=n), rng.integers(w.H, size=n),
+                         rng.integers(w.N, size=n)], 1)
+
+    def flops(w, rows):
+        nv = rows[:, 2] + 1 if w.causal else np.full(len(rows), w.N)
+        return float(4.0 * nv.sum() * w.d)
+
+    def timed(w, rows):
+        t0 = time.perf_counter()
+        oracle.attention_forward_rows(q64, k64, v64, w.causal, w.scale, rows)
+        return time.perf_counter() - t0
+
+    calib = max(32, 4 * n_thr)
+    cal_f = cal_t = 0.0
+    for w in ws:
+        rows = rows_for(w, calib)
+        cal_t += timed(w, rows)
+        cal_f += flops(w, rows)
+    rate = cal_f / max(cal_t, 1e-9)
+
+    total_f = total_t = 0.0
+    desc = []
+    for w in ws:
+        per_row = 4.0 * (w.N / 2 if w.causal else w.N) * w.d
+        n = int(min(w.B * w.H * w.N, max(calib, target_s / len(ws) * rate / per_row)))
+        rows = rows_for(w, n)
+        total_t += timed(w, rows)
+        total_f += flops(w, rows)
+        desc.append(f"{n} random rows of {w.name}")
+    return {
+        "value": round(total_f / total_t / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": n_thr,
+        "kind": "oracle",
+        "sample": "; ".join(desc) + f"; fp64, {total_t:.1f} s of oracle compute",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -11,4 +11,5 @@ from .oracle import (  # noqa: F401
     attention_backward,
     build,
     num_threads,
+    widen,
 )

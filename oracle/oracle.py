@@ -65,7 +65,7 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def _f64(x) -> np.ndarray:
+def widen(x) -> np.ndarray:
     """Exact widening to a contiguous float64 array (bf16/fp32 -> fp64 is exact)."""
     if hasattr(x, "detach"):  # torch tensor
         import torch
@@ -86,7 +86,7 @@ def _shape4(q):
 
 def attention_forward(q, k, v, causal: bool, scale: float):
     """Full forward pass. Returns (o [B,N,H,d], lse [B,H,N]) as float64 arrays."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    q, k, v = widen(q), widen(k), widen(v)
     B, N, H, d = _shape4(q)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one [B, N, H, d] shape")
@@ -105,7 +105,7 @@ def attention_forward_rows(q, k, v, causal: bool, scale: float, rows):
 
     Returns (o_rows [n, d], lse_rows [n]) as float64 arrays.
     """
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    q, k, v = widen(q), widen(k), widen(v)
     B, N, H, d = _shape4(q)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
     n = rows.shape[0]
@@ -125,7 +125,7 @@ def attention_backward(q, k, v, dout, causal: bool, scale: float, heads=None):
     heads: int array [n, 2] of (b, h).  Returns a dict of float64 arrays:
     dq, dk, dv [n, N, d]; lse, D [n, N].
     """
-    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    q, k, v, dout = widen(q), widen(k), widen(v), widen(dout)
     B, N, H, d = _shape4(q)
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(H)]
