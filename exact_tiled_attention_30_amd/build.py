@@ -25,6 +25,8 @@ HIPCC_FLAGS = [
     "-shared",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # fp32 atomicAdd -> hardware global_atomic_add_f32 (device memory is coarse-grained)
+    "-munsafe-fp-atomics",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]

@@ -34,6 +34,8 @@ int check_shape(int B, int H, int N, int d, float scale, size_t* elems, size_t* 
   if (!isfinite(scale)) return FA2_ERR_SCALE;
   const long double e = (long double)B * H * N * d;
   if (e > (long double)kMaxElems) return FA2_ERR_SHAPE;
+  // every launch size derived from the row count must fit 32-bit grids
+  if ((long double)B * H * N > 2147483647.0L) return FA2_ERR_SHAPE;
   // grid = B * H * ceil(N / 128) workgroups must fit the launch limit
   const long double grid = (long double)B * H * ((N + 127) / 128);
   if (grid > 2147483647.0L) return FA2_ERR_SHAPE;

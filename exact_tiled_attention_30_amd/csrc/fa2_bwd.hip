@@ -1,12 +1,371 @@
-// fa2_bwd.hip -- FlashAttention-2 backward pass for gfx950 (in progress).
+// fa2_bwd.hip -- FlashAttention-2 backward pass for gfx950.
+//
+// Structure from infra-guide page "6.2 FlashAttention V2 in depth", section 7:
+//   * P is not stored by the forward pass; it is recomputed from the saved
+//     logsumexp L (section 7.1): P = exp(scale * q.k - L).
+//   * The outer loop runs over key/value tiles: the workgroup that holds K_j,
+//     V_j accumulates dK_j and dV_j by itself with no atomics; dQ is summed
+//     across workgroups -- here with fp32 atomics into a workspace (section 7.2).
+//   * D_i = rowsum(dO_i * O_i) is computed once by a separate pre-processing
+//     kernel (section 7.3) instead of tile by tile inside the main loop.
+// Gradient formulas (lost in the page's extraction; the standard softmax
+// gradient): dV = P^T dO, dP = dO V^T, dS = P * (dP - D), dK = scale dS^T Q,
+// dQ = scale dS K.
+//
+// gfx950 mapping of the main kernel (bwd_kernel):
+//   * workgroup = 4 waves = 128 keys of one (batch, head); each wave owns 32
+//     keys and keeps their K and V rows in VGPRs (MFMA B operands) and their
+//     dK, dV accumulators in registers for the whole loop;
+//   * it walks 64-query tiles of Q and dO, staged in LDS in both row-major and
+//     transposed form (the MFMA operand orientations need both);
+//   * S = Q K^T and dP = dO V^T put the key on the accumulator column, i.e. on
+//     the lane, so P and dS feed the dV += P^T dO and dK += dS^T Q products
+//     straight from registers; dS also goes to LDS, from which the workgroup
+//     forms its dQ partial = dS K over its 128 keys and adds it atomically.
+#include <math.h>
+
 #include "fa2_device.hpp"
 #include "fa2_internal.hpp"
 
 namespace fa2 {
+namespace {
+
+constexpr int kBwdThreads = 256;
+constexpr int kBwdKeys = 128;    // keys per workgroup (4 waves x 32)
+constexpr int kBwdQueries = 64;  // queries per inner step
+
+// ---------------------------------------------------------------- B0 ----
+// D[b, h, i] = sum_c dO[b, i, h, c] * O[b, i, h, c] (fp32), and zero the dQ
+// accumulator row.  One 16-lane group per (b, i, h) row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_preprocess_kernel(
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+    float* __restrict__ delta, float* __restrict__ dq_acc, int H, int N, long long rows) {
+  constexpr int kLanesPerRow = 16;
+  constexpr int kElemsPerLane = D / kLanesPerRow;  // 8 (d=128) or 4 (d=64)
+  const long long row = (long long)blockIdx.x * (256 / kLanesPerRow) + threadIdx.x / kLanesPerRow;
+  const int sub = threadIdx.x % kLanesPerRow;
+  float acc = 0.f;
+  if (row < rows) {
+    const size_t base = (size_t)row * D + sub * kElemsPerLane;  // row = (b*N + i)*H + h
+    if constexpr (kElemsPerLane == 8) {
+      const u32x4 a = *(const u32x4*)(o + base);
+      const u32x4 g = *(const u32x4*)(dout + base);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc += __uint_as_float(a[t] << 16) * __uint_as_float(g[t] << 16);
+        acc += __uint_as_float(a[t] & 0xffff0000u) * __uint_as_float(g[t] & 0xffff0000u);
+      }
+      *(f32x4*)(dq_acc + base) = f32x4{};
+      *(f32x4*)(dq_acc + base + 4) = f32x4{};
+    } else {
+      const u32x2 a = *(const u32x2*)(o + base);
+      const u32x2 g = *(const u32x2*)(dout + base);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        acc += __uint_as_float(a[t] << 16) * __uint_as_float(g[t] << 16);
+        acc += __uint_as_float(a[t] & 0xffff0000u) * __uint_as_float(g[t] & 0xffff0000u);
+      }
+      *(f32x4*)(dq_acc + base) = f32x4{};
+    }
+  }
+  // reduce over the 16 lanes of the row
+#pragma unroll
+  for (int off = kLanesPerRow / 2; off > 0; off /= 2) acc += __shfl_xor(acc, off, kWave);
+  if (row < rows && sub == 0) {
+    const long long h = row % H;
+    const long long i = (row / H) % N;
+    const long long b = row / ((long long)H * N);
+    delta[(b * H + h) * N + i] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- B2 ----
+// dq = bf16(dq_acc), 8 elements per thread.
+__global__ __launch_bounds__(256) void bwd_convert_dq_kernel(const float* __restrict__ dq_acc,
+                                                             uint16_t* __restrict__ dq,
+                                                             long long n8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = *(const f32x4*)(dq_acc + 8 * i);
+  const f32x4 b = *(const f32x4*)(dq_acc + 8 * i + 4);
+  const bf16x8 r = to_bf16x8(f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+  *(u32x4*)(dq + 8 * i) = as_u32x4(r);
+}
+
+// ---------------------------------------------------------------- B1 ----
+template <int D>
+struct BwdCfg {
+  static constexpr int kQStride = D + 8;                 // row-major Q / dO tiles
+  static constexpr int kQTStride = kBwdQueries + 4;      // transposed Q / dO tiles
+  static constexpr int kSStride = kBwdKeys + 8;          // dS tile [query][key]
+  static constexpr int kKTStride = kBwdKeys + 8;         // K^T [d][key]
+  static constexpr int kRowsPerUnit = D / 32;            // Q rows per staging unit
+  static constexpr int kKeysPerUnit = D / 16;            // keys per K^T staging unit
+  static constexpr int kDqTilesPerWave = D / 64;         // 32x32 dQ tiles per wave
+  static_assert((kBwdQueries / kRowsPerUnit) * (D / 8) == kBwdThreads, "Q staging");
+  static_assert((kBwdKeys / kKeysPerUnit) * (D / 8) == kBwdThreads, "K^T staging");
+};
+
+template <int D>
+struct BwdSmem {
+  using C = BwdCfg<D>;
+  uint16_t qs[kBwdQueries * C::kQStride];
+  uint16_t dos[kBwdQueries * C::kQStride];
+  uint16_t qt[D * C::kQTStride];
+  uint16_t dot[D * C::kQTStride];
+  uint16_t dss[kBwdQueries * C::kSStride];
+  uint16_t kt[D * C::kKTStride];
+  float lse2[kBwdQueries];
+  float dl[kBwdQueries];
+};
+
+// Two bf16 from element i of two 8-element rows, packed (row a low half).
+__device__ __forceinline__ uint32_t pack_pair(const u32x4& a, const u32x4& b, int i) {
+  const uint32_t x = a[i / 2], y = b[i / 2];
+  return (i & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+}
+
+// Stage rows [r0, r0 + KPU) x [8*dc, 8*dc + 8) of a [B,N,H,D] tensor slice:
+// row-major into `rm` (unless null) and transposed into `tr`.
+template <int D, int KPU>
+__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, size_t head,
+                                           size_t tok, int n0, int N, int r0, int dc,
+                                           uint16_t* rm, int rm_stride, uint16_t* tr,
+                                           int tr_stride) {
+  u32x4 x[KPU];
+#pragma unroll
+  for (int kk = 0; kk < KPU; ++kk) {
+    const int n = n0 + r0 + kk;
+    x[kk] = u32x4{0u, 0u, 0u, 0u};
+    if (n < N) x[kk] = *(const u32x4*)(src + head + (size_t)n * tok + dc * 8);
+    if (rm) *(u32x4*)(rm + (r0 + kk) * rm_stride + dc * 8) = x[kk];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint16_t* dst = tr + (dc * 8 + i) * tr_stride + r0;
+#pragma unroll
+    for (int kk = 0; kk < KPU; kk += 2) *(uint32_t*)(dst + kk) = pack_pair(x[kk], x[kk + 1], i);
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dq_acc,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int H, int N, int n_ktiles, int grid,
+    float c, float scale) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) BwdSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane % 32, hi = lane / 32;
+
+  const int logical = xcd_contiguous_id(blockIdx.x, grid);
+  const int bh = logical / n_ktiles;
+  const int kt_idx = logical % n_ktiles;  // heaviest (first) key tiles first under causal
+  const int b = bh / H, hh = bh % H;
+  const int j0 = kt_idx * kBwdKeys;
+  const int kw0 = j0 + wave * 32;  // first key of this wave
+  const int my_key = kw0 + l32;    // the key this lane's accumulator column holds
+  const size_t tok = (size_t)H * D;
+  const size_t head = (size_t)b * N * tok + (size_t)hh * D;
+  const size_t rowstat = ((size_t)b * H + hh) * N;
+
+  // K and V rows of this lane's key: B operands (column = key, 8 d per slot group)
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) {
+    u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+    if (my_key < N) {
+      xk = *(const u32x4*)(k + head + (size_t)my_key * tok + cc * 16 + hi * 8);
+      xv = *(const u32x4*)(v + head + (size_t)my_key * tok + cc * 16 + hi * 8);
+    }
+    kf[cc] = as_bf16x8(xk);
+    vf[cc] = as_bf16x8(xv);
+  }
+  // K^T of the workgroup's 128 keys, for dQ = dS K
+  {
+    constexpr int KPU = C::kKeysPerUnit;
+    const int r0 = (tid / (D / 8)) * KPU, dc = tid % (D / 8);
+    stage_rows<D, KPU>(k, head, tok, j0, N, r0, dc, nullptr, 0, sm.kt, C::kKTStride);
+  }
+
+  f32x16 dk_acc[D / 32], dv_acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    dk_acc[dt] = f32x16{};
+    dv_acc[dt] = f32x16{};
+  }
+
+  const int n_qtiles = (N + kBwdQueries - 1) / kBwdQueries;
+  const int it0 = CAUSAL ? j0 / kBwdQueries : 0;
+  for (int it = it0; it < n_qtiles; ++it) {
+    const int q0 = it * kBwdQueries;
+    // ---- stage Q, dO (row-major + transposed), L*log2e and D
+    {
+      constexpr int KPU = C::kRowsPerUnit;
+      const int r0 = (tid / (D / 8)) * KPU, dc = tid % (D / 8);
+      stage_rows<D, KPU>(q, head, tok, q0, N, r0, dc, sm.qs, C::kQStride, sm.qt, C::kQTStride);
+      stage_rows<D, KPU>(dout, head, tok, q0, N, r0, dc, sm.dos, C::kQStride, sm.dot,
+                         C::kQTStride);
+      if (tid < kBwdQueries) {
+        const int qi = q0 + tid;
+        sm.lse2[tid] = qi < N ? lse[rowstat + qi] * kLog2e : 0.f;
+        sm.dl[tid] = qi < N ? delta[rowstat + qi] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // ---- S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x16{};
+      dp[t] = f32x16{};
+    }
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 aq = *(const bf16x8*)(sm.qs + (t * 32 + l32) * C::kQStride + cc * 16 + hi * 8);
+        const bf16x8 ad = *(const bf16x8*)(sm.dos + (t * 32 + l32) * C::kQStride + cc * 16 + hi * 8);
+        s[t] = mfma32(aq, kf[cc], s[t]);
+        dp[t] = mfma32(ad, vf[cc], dp[t]);
+      }
+    }
+
+    // ---- P = exp2(S*c - L*log2e), dS = P * (dP - D); masked entries are 0
+    const bool need_mask = (CAUSAL && kw0 + 31 > q0) || (q0 + kBwdQueries > N) || (kw0 + 32 > N);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = t * 32 + 8 * g + 4 * hi;  // local query of register 4*g
+        const f32x4 l4 = *(const f32x4*)(sm.lse2 + qr);
+        const f32x4 d4 = *(const f32x4*)(sm.dl + qr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = fast_exp2(fmaf(s[t][r], c, -l4[e]));
+          if (need_mask) {
+            const int query = q0 + qr + e;
+            const bool visible = query < N && my_key < N && (!CAUSAL || my_key <= query);
+            if (!visible) p = 0.f;
+          }
+          s[t][r] = p;
+          dp[t][r] = p * (dp[t][r] - d4[e]);
+        }
+      }
+    }
+
+    // ---- dV += P^T dO and dK += dS^T Q (contraction over the 64 queries).
+    // Slot t of lane half hi pairs with query 16*cc + 8*(t/4) + 4*hi + t%4.
+#pragma unroll
+    for (int cc = 0; cc < kBwdQueries / 16; ++cc) {
+      const int r0 = 8 * (cc % 2);
+      const f32x16& sv = s[cc / 2];
+      const f32x16& dsv = dp[cc / 2];
+      const bf16x8 pf = to_bf16x8(f32x8{sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
+                                        sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]});
+      const bf16x8 dsf = to_bf16x8(f32x8{dsv[r0], dsv[r0 + 1], dsv[r0 + 2], dsv[r0 + 3],
+                                         dsv[r0 + 4], dsv[r0 + 5], dsv[r0 + 6], dsv[r0 + 7]});
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const uint16_t* dr = sm.dot + (dt * 32 + l32) * C::kQTStride + cc * 16 + 4 * hi;
+        const u32x2 dlo = *(const u32x2*)dr, dup = *(const u32x2*)(dr + 8);
+        dv_acc[dt] = mfma32(pf, as_bf16x8(u32x4{dlo[0], dlo[1], dup[0], dup[1]}), dv_acc[dt]);
+        const uint16_t* qr = sm.qt + (dt * 32 + l32) * C::kQTStride + cc * 16 + 4 * hi;
+        const u32x2 qlo = *(const u32x2*)qr, qup = *(const u32x2*)(qr + 8);
+        dk_acc[dt] = mfma32(dsf, as_bf16x8(u32x4{qlo[0], qlo[1], qup[0], qup[1]}), dk_acc[dt]);
+      }
+    }
+
+    // ---- dS (bf16) -> LDS [query][key] for the dQ product
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = t * 32 + acc_row(r, hi);
+        sm.dss[ql * C::kSStride + wave * 32 + l32] = to_bf16_bits(dp[t][r]);
+      }
+    __syncthreads();
+
+    // ---- dQ partial = scale * dS K over this workgroup's keys, added atomically
+#pragma unroll
+    for (int u = 0; u < C::kDqTilesPerWave; ++u) {
+      const int tile = wave * C::kDqTilesPerWave + u;  // 0 .. 2*D/32-1
+      const int t = tile % 2, dt = tile / 2;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < kBwdKeys / 16; ++cc) {
+        const bf16x8 a = *(const bf16x8*)(sm.dss + (t * 32 + l32) * C::kSStride + cc * 16 + hi * 8);
+        const bf16x8 bk = *(const bf16x8*)(sm.kt + (dt * 32 + l32) * C::kKTStride + cc * 16 + hi * 8);
+        acc = mfma32(a, bk, acc);
+      }
+      // accumulator: column = d (lane), rows = queries
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int query = q0 + t * 32 + acc_row(r, hi);
+        if (query < N)
+          atomicAdd(dq_acc + head + (size_t)query * tok + dt * 32 + l32, scale * acc[r]);
+      }
+    }
+    __syncthreads();  // LDS tiles are rewritten by the next step
+  }
+
+  // ---- dK = scale * acc, dV = acc; accumulator column = d (lane), rows = keys
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kw0 + acc_row(r, hi);
+      if (key < N) {
+        const size_t off = head + (size_t)key * tok + dt * 32 + l32;
+        dk[off] = to_bf16_bits(scale * dk_acc[dt][r]);
+        dv[off] = to_bf16_bits(dv_acc[dt][r]);
+      }
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdParams& p) {
+  const long long rows = (long long)p.B * p.N * p.H;
+  (void)hipGetLastError();
+  // B0: D vector and dQ accumulator reset
+  {
+    const long long blocks = (rows + 15) / 16;
+    hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)blocks), dim3(256), 0,
+                       p.stream, (const uint16_t*)p.o, (const uint16_t*)p.dout, p.delta,
+                       p.dq_acc, p.H, p.N, rows);
+  }
+  // B1: main KV-outer kernel
+  {
+    const int n_ktiles = (p.N + kBwdKeys - 1) / kBwdKeys;
+    const long long grid = (long long)p.B * p.H * n_ktiles;
+    const float c = (float)((double)p.scale * 1.4426950408889634);
+    hipLaunchKernelGGL((bwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kBwdThreads), 0,
+                       p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
+                       (const uint16_t*)p.v, (const uint16_t*)p.dout, p.lse, p.delta,
+                       p.dq_acc, (uint16_t*)p.dk, (uint16_t*)p.dv, p.H, p.N, n_ktiles,
+                       (int)grid, c, p.scale);
+  }
+  // B2: dQ to bf16
+  {
+    const long long n8 = rows * D / 8;
+    hipLaunchKernelGGL(bwd_convert_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                       p.stream, p.dq_acc, (uint16_t*)p.dq, n8);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_bwd(const BwdParams& p) {
-  (void)p;
-  return hipErrorNotSupported;
+  if (p.d == 64) return p.causal ? launch_bwd_t<64, true>(p) : launch_bwd_t<64, false>(p);
+  return p.causal ? launch_bwd_t<128, true>(p) : launch_bwd_t<128, false>(p);
 }
 
 }  // namespace fa2

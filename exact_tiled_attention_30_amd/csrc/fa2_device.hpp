@@ -49,6 +49,10 @@ __device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) {
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
   return __builtin_convertvector(x, bf16x4);
 }
+// Round-to-nearest-even fp32 -> bf16 bit pattern.
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
 
 // Value of the same register in the partner lane l ^ 32 (the other half of
 // the wave holds the other half of each 32x32 accumulator column).
