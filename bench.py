@@ -75,11 +75,39 @@ def parse_args():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (for scaling the "
+                        "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    """A plain device-to-device copy of known size, timed; under rocprofv3
+    --pmc its FETCH_SIZE and WRITE_SIZE give the counters' scale factor."""
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps,
+                      "ms": round(ms, 4), "GB_per_s": round(2 * n / ms / 1e6, 1)}), flush=True)
 
 
 def main():
     args = parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

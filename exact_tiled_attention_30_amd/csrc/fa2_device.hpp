@@ -60,6 +60,21 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, kWave);
 }
 
+// max / sum of a value over the lane pair (l, l ^ 32) with one
+// v_permlane32_swap: its two results are the two halves' values, in some
+// order, in every lane -- the symmetric combinations below do not depend on
+// which is which.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
 }

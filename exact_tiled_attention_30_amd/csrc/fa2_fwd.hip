@@ -34,6 +34,7 @@
 //    the ragged end of the sequence) run the element mask.
 #include <math.h>
 
+
 #include "fa2_device.hpp"
 #include "fa2_internal.hpp"
 
@@ -42,9 +43,9 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int BC>
+template <int D, int BC, int WAVES>
 struct FwdCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = WAVES;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kRowsPerWave = 32;
   static constexpr int BR = kWaves * kRowsPerWave;
@@ -55,13 +56,14 @@ struct FwdCfg {
   static constexpr int kVStride = BC + 4;
   static constexpr int kKTile = BC * kKStride;
   static constexpr int kVTile = D * kVStride;
-  // Global -> LDS staging work per thread.
-  static constexpr int kKChunks = BC * D / 8 / kThreads;  // 16-byte K chunks
-  static constexpr int kKeysPerUnit = ((BC / 4) * (D / 8)) % kThreads == 0 ? 4 : 2;
-  static constexpr int kVUnits = (BC / kKeysPerUnit) * (D / 8) / kThreads;
+  // Global -> LDS staging: K in 16-byte chunks; V in units of KPU keys x 8 d
+  // (transposed on the way into LDS).  Threads beyond the work idle.
+  static constexpr int kKChunkCount = BC * D / 8;
+  static constexpr int kKChunks = (kKChunkCount + kThreads - 1) / kThreads;
+  static constexpr int kKeysPerUnit = (BC / 4) * (D / 8) >= kThreads ? 4 : 2;
+  static constexpr int kVUnitCount = (BC / kKeysPerUnit) * (D / 8);
+  static constexpr int kVUnits = (kVUnitCount + kThreads - 1) / kThreads;
   static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
-  static_assert(kKChunks * kThreads * 8 == BC * D, "K staging must cover the tile");
-  static_assert(kVUnits * kThreads * kKeysPerUnit * 8 == BC * D, "V staging must cover the tile");
 };
 
 // Two bf16 from element i of two 8-element rows, packed (row a in the low half).
@@ -70,12 +72,12 @@ __device__ __forceinline__ uint32_t pack_col(const u32x4& a, const u32x4& b, int
   return (i & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
 }
 
-template <int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_kernel(
+template <int D, int BC, int WAVES, int OCC, bool CAUSAL, int SCHED = 0>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC))) void fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int H, int N, int n_qtiles, int grid, float c, uint32_t q_sign) {
-  using C = FwdCfg<D, BC>;
+    int H, int N, int n_qtiles, int grid, float c, uint32_t q_and, uint32_t q_xor) {
+  using C = FwdCfg<D, BC, WAVES>;
   constexpr int KPU = C::kKeysPerUnit;
   __shared__ __attribute__((aligned(16))) uint16_t ks[2 * C::kKTile];
   __shared__ __attribute__((aligned(16))) uint16_t vt[2 * C::kVTile];
@@ -104,7 +106,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(
     for (int cc = 0; cc < D / 16; ++cc) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (my_q < N) x = *(const u32x4*)(qp + 16 * cc);
-      x ^= q_sign;  // negative scale: negate Q (exact), use |scale|
+      // scale < 0: negate Q (exact) and use |scale|; scale == 0: zero Q and
+      // use c = 1, so every visible score is exactly 0 and P exactly 1
+      x = (x & q_and) ^ q_xor;
       qf[cc] = as_bf16x8(x);
     }
   }
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(
   // ---- K/V staging through registers into the double-buffered LDS tiles.
   u32x4 kreg[C::kKChunks];
   u32x4 vreg[C::kVUnits][KPU];
-  auto load_tile = [&](int jt) {
+  auto load_tile = [&](int jt) __attribute__((always_inline)) {
     const int kv0 = jt * BC;
 #pragma unroll
     for (int it = 0; it < C::kKChunks; ++it) {
@@ -123,7 +127,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(
       const int key = ci / (D / 8), dc = ci % (D / 8);
       const int gk = kv0 + key;
       kreg[it] = u32x4{0u, 0u, 0u, 0u};
-      if (gk < N) kreg[it] = *(const u32x4*)(k + head + (size_t)gk * tok + dc * 8);
+      if (ci < C::kKChunkCount && gk < N)
+        kreg[it] = *(const u32x4*)(k + head + (size_t)gk * tok + dc * 8);
     }
 #pragma unroll
     for (int it = 0; it < C::kVUnits; ++it) {
@@ -133,23 +138,25 @@ __global__ __launch_bounds__(256) void fwd_kernel(
       for (int kk = 0; kk < KPU; ++kk) {
         const int gk = kv0 + kg * KPU + kk;
         vreg[it][kk] = u32x4{0u, 0u, 0u, 0u};
-        if (gk < N) vreg[it][kk] = *(const u32x4*)(v + head + (size_t)gk * tok + dc * 8);
+        if (ui < C::kVUnitCount && gk < N)
+          vreg[it][kk] = *(const u32x4*)(v + head + (size_t)gk * tok + dc * 8);
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
     uint16_t* kd = ks + buf * C::kKTile;
 #pragma unroll
     for (int it = 0; it < C::kKChunks; ++it) {
       const int ci = tid + it * C::kThreads;
       const int key = ci / (D / 8), dc = ci % (D / 8);
-      *(u32x4*)(kd + key * C::kKStride + dc * 8) = kreg[it];
+      if (ci < C::kKChunkCount) *(u32x4*)(kd + key * C::kKStride + dc * 8) = kreg[it];
     }
     uint16_t* vd = vt + buf * C::kVTile;
 #pragma unroll
     for (int it = 0; it < C::kVUnits; ++it) {
       const int ui = tid + it * C::kThreads;
       const int kg = ui / (D / 8), dc = ui % (D / 8);
+      if (ui >= C::kVUnitCount) continue;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint16_t* dst = vd + (dc * 8 + i) * C::kVStride + kg * KPU;
@@ -184,17 +191,37 @@ __global__ __launch_bounds__(256) void fwd_kernel(
       const uint16_t* kb = ks + buf * C::kKTile;
       const uint16_t* vb = vt + buf * C::kVTile;
 
-      // S^T = K_j Q_i^T (scores of this lane's query against BC keys)
+      // S^T = K_j Q_i^T (scores of this lane's query against BC keys).  The K
+      // fragments are read kPrefetch MFMAs ahead of their use so LDS latency
+      // hides behind the MFMA pipeline.
+      constexpr int kSteps = (D / 16) * (BC / 32);
+      constexpr int kPrefetch = 4;
       f32x16 s[BC / 32];
 #pragma unroll
       for (int kt = 0; kt < BC / 32; ++kt) s[kt] = f32x16{};
+      auto kload = [&](int i) __attribute__((always_inline)) {
+        const int cc = i / (BC / 32), kt = i % (BC / 32);
+        return *(const bf16x8*)(kb + (kt * 32 + l32) * C::kKStride + cc * 16 + hi * 8);
+      };
+      bf16x8 kring[kPrefetch];
 #pragma unroll
-      for (int cc = 0; cc < D / 16; ++cc) {
+      for (int i = 0; i < kPrefetch; ++i) kring[i] = kload(i);
 #pragma unroll
-        for (int kt = 0; kt < BC / 32; ++kt) {
-          const bf16x8 a = *(const bf16x8*)(kb + (kt * 32 + l32) * C::kKStride + cc * 16 + hi * 8);
-          s[kt] = mfma32(a, qf[cc], s[kt]);
+      for (int i = 0; i < kSteps; ++i) {
+        const int cc = i / (BC / 32), kt = i % (BC / 32);
+        const bf16x8 a = kring[i % kPrefetch];
+        if (i + kPrefetch < kSteps) kring[i % kPrefetch] = kload(i + kPrefetch);
+        s[kt] = mfma32(a, qf[cc], s[kt]);
+      }
+      if constexpr (SCHED >= 1) {
+        // keep kPrefetch K reads in flight ahead of the MFMA that uses them
+        __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);
+#pragma unroll
+        for (int i = 0; i < kSteps - kPrefetch; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
       }
 
       // element mask on diagonal-crossing and ragged tiles only
@@ -210,13 +237,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(
           }
       }
 
-      // online softmax statistics
+      // online softmax statistics: tile max; the reference moves only when a
+      // row's max rises by more than kRescaleSlack
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < BC / 32; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      mx = fmaxf(mx, swap_halves(mx));
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
+      mx = pair_max(mx);
       const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
       if (wave_any(mt > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, mt);
@@ -227,42 +255,58 @@ __global__ __launch_bounds__(256) void fwd_kernel(
         m_run = m_new;
       }
       const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-      float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < BC / 32; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(s[kt][r], c, -mref));
-          if (need_mask && s[kt][r] == -INFINITY) p = 0.f;
-          s[kt][r] = p;
-          rs += p;
-        }
-      l_part += rs;
 
-      // O^T += V_j^T P^T: the P^T operand is the S^T accumulator, converted.
-      // Contraction slot t of lane half hi pairs with key
-      // 16*cc + 8*(t/4) + 4*hi + t%4 in both operands.
-#pragma unroll
-      for (int cc = 0; cc < BC / 16; ++cc) {
+      // P = exp2(S*c - m) and O^T += V_j^T P^T.  P for key chunk cc+1 is
+      // formed while the MFMAs of chunk cc run.  Contraction slot t of lane
+      // half hi pairs with key 16*cc + 8*(t/4) + 4*hi + t%4 in both operands.
+      float rs = 0.f;
+      auto chunk_p = [&](int cc) __attribute__((always_inline)) {
+        // c > 0, so a masked score of -inf gives exp2(-inf) = 0
         const f32x16& sv = s[cc / 2];
         const int r0 = 8 * (cc % 2);
-        const bf16x8 pf = to_bf16x8(f32x8{sv[r0 + 0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3],
-                                          sv[r0 + 4], sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]});
+        f32x8 pv;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          pv[t] = fast_exp2(fmaf(sv[r0 + t], c, -mref));
+          rs += pv[t];
+        }
+        return to_bf16x8(pv);
+      };
+      bf16x8 pf = chunk_p(0);
+#pragma unroll
+      for (int cc = 0; cc < BC / 16; ++cc) {
+        u32x4 vfrag[D / 32];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const uint16_t* vr = vb + (dt * 32 + l32) * C::kVStride + cc * 16 + 4 * hi;
           const u32x2 lo = *(const u32x2*)vr;
           const u32x2 up = *(const u32x2*)(vr + 8);
-          oacc[dt] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], up[0], up[1]}), pf, oacc[dt]);
+          vfrag[dt] = u32x4{lo[0], lo[1], up[0], up[1]};
+        }
+        const bf16x8 pcur = pf;
+        if (cc + 1 < BC / 16) pf = chunk_p(cc + 1);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          oacc[dt] = mfma32(as_bf16x8(vfrag[dt]), pcur, oacc[dt]);
+        if constexpr (SCHED >= 2) {
+          // this chunk's V reads first, then each MFMA followed by a slice of
+          // the next chunk's softmax VALU work
+          __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 1);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, 28 / (D / 32), 1);
+          }
         }
       }
+      l_part += rs;
     }
     if (jt + 1 < n_kv) store_tile(buf ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: one division by l per row, bf16 O, natural-log L
-  const float l = l_part + swap_halves(l_part);
+  const float l = pair_sum(l_part);
   const float inv = 1.0f / l;
   if (my_q < N) {
     uint16_t* op = o + head + (size_t)my_q * tok;
@@ -278,29 +322,32 @@ __global__ __launch_bounds__(256) void fwd_kernel(
   }
 }
 
-template <int D, int BC, bool CAUSAL>
+template <int D, int BC, int WAVES, int OCC, bool CAUSAL, int SCHED = 0>
 hipError_t launch_fwd_t(const FwdParams& p) {
-  using C = FwdCfg<D, BC>;
+  using C = FwdCfg<D, BC, WAVES>;
   const int n_qtiles = (p.N + C::BR - 1) / C::BR;
   const long long grid = (long long)p.B * p.H * n_qtiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const float c = (float)(fabs((double)p.scale) * 1.4426950408889634);
-  const uint32_t q_sign = p.scale < 0.f ? 0x80008000u : 0u;
+  const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
+  const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
+  const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
   (void)hipGetLastError();
-  hipLaunchKernelGGL((fwd_kernel<D, BC, CAUSAL>), dim3((unsigned)grid), dim3(C::kThreads), 0,
+  hipLaunchKernelGGL((fwd_kernel<D, BC, WAVES, OCC, CAUSAL, SCHED>), dim3((unsigned)grid), dim3(C::kThreads), 0,
                      p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
-                     (uint16_t*)p.o, p.lse, p.H, p.N, n_qtiles, (int)grid, c, q_sign);
+                     (uint16_t*)p.o, p.lse, p.H, p.N, n_qtiles, (int)grid, c, q_and, q_xor);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p) {
+  // Tile shapes chosen by measurement on MI355X (K/V tile BC, waves per
+  // workgroup, minimum waves per SIMD); every one is parity-tested.
   if (p.d == 64) {
-    return p.causal ? launch_fwd_t<64, 64, true>(p) : launch_fwd_t<64, 64, false>(p);
+    return p.causal ? launch_fwd_t<64, 64, 4, 2, true>(p) : launch_fwd_t<64, 128, 8, 2, false>(p);
   }
-  return p.causal ? launch_fwd_t<128, 64, true>(p) : launch_fwd_t<128, 64, false>(p);
+  return p.causal ? launch_fwd_t<128, 64, 8, 2, true>(p) : launch_fwd_t<128, 64, 8, 2, false>(p);
 }
 
 }  // namespace fa2
