@@ -322,6 +322,282 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant (the production forward kernel).
+//
+// K and V tiles move HBM/L2 -> LDS with global_load_lds_dwordx4: lane L of a
+// wave deposits its 16 bytes at LDS base + 16*L, so no VGPRs, no ds_write and
+// no VALU packing are spent on staging.  Rows are stored unpadded (D*2 bytes)
+// with the 16-byte chunks of each row permuted by an XOR swizzle, chosen per
+// tensor so the MFMA operand reads below are free of bank conflicts; the
+// loading lane fetches whichever global chunk belongs at its LDS slot.
+//  * K operand (S^T = K Q^T): lane reads 16 bytes of key row kt*32 + l%32.
+//  * V^T operand (O^T = V^T P^T): two ds_read_b64_tr_b16.  Within each group
+//    of 16 lanes, output lane 4a+b receives element b of the 8-byte chunks
+//    addressed by lanes a, 4+a, 8+a, 12+a (pinned by a probe on gfx950); so
+//    when lane 4i+a addresses 4 consecutive d of key row key_i, every output
+//    lane holds one d column across 4 keys -- the transposed fragment -- read
+//    straight from the row-major V tile.
+// LDS buffers are separate arrays picked at compile time (the tile loop is
+// unrolled by two) so the compiler can tell the in-flight LDS DMA into one
+// buffer from the reads of the other.
+template <int D>
+struct DlSwz {
+  // XOR applied to the 16-byte chunk index of row r
+  __device__ static constexpr int k(int r) { return D == 128 ? (r % 16) : ((r / 2) % 8); }
+  __device__ static constexpr int v(int r) { return D == 128 ? 4 * (r % 4) : 4 * ((r / 2) % 2); }
+};
+
+template <int D, int BC, int W, int STAGES, bool CAUSAL>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 1))) void fwd_dl_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
+    int H, int N, int n_qtiles, int grid, float c, uint32_t q_and, uint32_t q_xor) {
+  constexpr int kWaves = W;
+  constexpr int BR = kWaves * 32;
+  constexpr int RB = D * 2;                 // bytes per LDS row
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;            // rows per 1 KB load instruction
+  constexpr int TILE = BC * RB;             // bytes per K or V tile
+  constexpr int NI = TILE / 1024;           // load instructions per tile and tensor
+  constexpr int NIW = NI / kWaves;          // ... per wave
+  static_assert(NI % kWaves == 0 && NIW >= 1, "tile must split evenly over the waves");
+  using SW = DlSwz<D>;
+  static_assert(STAGES == 2 || STAGES == 3, "pipeline depth");
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb2[STAGES > 2 ? TILE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb2[STAGES > 2 ? TILE : 16];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane % 32, hi = lane / 32;
+
+  const int logical = xcd_contiguous_id(blockIdx.x, grid);
+  const int bh = logical / n_qtiles;
+  int qt = logical % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  const int b = bh / H, hh = bh % H;
+  const int q0 = qt * BR;
+  const int qw0 = q0 + wave * 32;
+  const int my_q = qw0 + l32;
+  const size_t tok = (size_t)H * D;
+  const size_t head = (size_t)b * N * tok + (size_t)hh * D;
+
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qp = q + head + (size_t)min(my_q, N - 1) * tok + 8 * hi;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      u32x4 x = *(const u32x4*)(qp + 16 * cc);
+      if (my_q >= N) x = u32x4{0u, 0u, 0u, 0u};
+      x = (x & q_and) ^ q_xor;
+      qf[cc] = as_bf16x8(x);
+    }
+  }
+
+  const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_kv = (kv_len + BC - 1) / BC;
+
+  // Per-lane byte offsets of the chunks this lane deposits, relative to the
+  // tile's first key row; the tile base is a scalar pointer.
+  uint32_t koff[NIW], voff[NIW];
+  int lrow[NIW];
+#pragma unroll
+  for (int u = 0; u < NIW; ++u) {
+    const int m = wave * NIW + u;
+    const int r = m * RPI + lane / CPR, slot = lane % CPR;
+    lrow[u] = r;
+    koff[u] = (uint32_t)(r * tok * 2) + (uint32_t)((slot ^ SW::k(r)) * 16);
+    voff[u] = (uint32_t)(r * tok * 2) + (uint32_t)((slot ^ SW::v(r)) * 16);
+  }
+  // issue the direct loads of tile jt (rows past N repeat row N-1)
+  auto issue = [&](int jt, uint8_t* kd, uint8_t* vd) __attribute__((always_inline)) {
+    const int kv0 = jt * BC;
+    const uint8_t* kbase = (const uint8_t*)(k + head + (size_t)kv0 * tok);
+    const uint8_t* vbase = (const uint8_t*)(v + head + (size_t)kv0 * tok);
+    const bool whole = kv0 + BC <= N;
+#pragma unroll
+    for (int u = 0; u < NIW; ++u) {
+      const int m = wave * NIW + u;
+      uint32_t ko = koff[u], vo = voff[u];
+      if (!whole) {
+        const uint32_t back = (uint32_t)(max(kv0 + lrow[u] - (N - 1), 0) * tok * 2);
+        ko -= back;
+        vo -= back;
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(kbase + ko),
+          (void __attribute__((address_space(3)))*)(kd + m * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(vbase + vo),
+          (void __attribute__((address_space(3)))*)(vd + m * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+
+  auto tile = [&](int jt, const uint8_t* kb, const uint8_t* vb) __attribute__((always_inline)) {
+    const int kv0 = jt * BC;
+    f32x16 s[BC / 32];
+#pragma unroll
+    for (int kt = 0; kt < BC / 32; ++kt) s[kt] = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc)
+#pragma unroll
+      for (int kt = 0; kt < BC / 32; ++kt) {
+        const int r = kt * 32 + l32;
+        const bf16x8 a = *(const bf16x8*)(kb + r * RB + ((cc * 2 + hi) ^ SW::k(r)) * 16);
+        s[kt] = mfma32(a, qf[cc], s[kt]);
+      }
+    {
+      // keep four K reads in flight ahead of the MFMAs that consume them
+      constexpr int kSteps = (D / 16) * (BC / 32), kAhead = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+      for (int i = 0; i < kSteps - kAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+    }
+
+    const bool need_mask = (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N);
+    if (need_mask) {
+#pragma unroll
+      for (int kt = 0; kt < BC / 32; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kt * 32 + acc_row(r, hi);
+          const bool visible = key < N && (!CAUSAL || key <= my_q);
+          if (!visible) s[kt][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < BC / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
+    mx = pair_max(mx);
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+    if (wave_any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+
+    // V^T fragment addresses: this lane supplies row 16*cc + 8*u + 4*hi + i,
+    // columns dt*32 + 16*(g%2) + 4*a .. +3 (g = lane/16, i = (lane%16)/4, a = lane%4)
+    const int g16 = lane / 16, i4 = (lane % 16) / 4, a4 = lane % 4;
+    float rs = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < BC / 16; ++cc) {
+      const f32x16& sv = s[cc / 2];
+      const int r0 = 8 * (cc % 2);
+      f32x8 p8;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        p8[t] = fast_exp2(fmaf(sv[r0 + t], c, -mref));
+        rs += p8[t];
+      }
+      const bf16x8 pcur = to_bf16x8(p8);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int col = dt * 32 + 16 * (g16 % 2) + 4 * a4;
+        u32x2 part[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int R = 16 * cc + 8 * u + 4 * hi + i4;
+          const uint8_t* addr = vb + R * RB + (((col / 8) ^ SW::v(R)) * 16) + (col % 8) * 2;
+          part[u] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (short __attribute__((ext_vector_type(4))) __attribute__((address_space(3)))*)addr));
+        }
+        oacc[dt] = mfma32(as_bf16x8(u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}), pcur,
+                          oacc[dt]);
+      }
+    }
+    l_part += rs;
+  };
+
+  // STAGES-deep LDS pipeline.  At step jt the DMA for tile jt+STAGES-1 is
+  // issued into the buffer tile jt-1 used (its readers passed the barrier
+  // that ended step jt-1); every step issues one batch (the tile index is
+  // clamped at the end), so the wait before each barrier is "all but the
+  // newest STAGES-2 batches" -- which leaves tile jt+1 landed.
+  static_assert(2 * NIW * (STAGES - 1) <= 15, "vmcnt immediate");
+  constexpr int kWaitStep = 0x0F70 | (2 * NIW * (STAGES - 2));
+  if (n_kv > 0) {
+    issue(0, kb0, vb0);
+    if constexpr (STAGES > 2) issue(min(1, n_kv - 1), kb1, vb1);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitStep);  // tile 0 has landed
+  __syncthreads();
+
+  auto step = [&](int jt, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn)
+      __attribute__((always_inline)) {
+    issue(min(jt + STAGES - 1, n_kv - 1), kn, vn);
+    if (!CAUSAL || jt * BC <= qw0 + 31) tile(jt, kc, vc);
+    __builtin_amdgcn_s_waitcnt(kWaitStep);  // tile jt+1 has landed
+    __syncthreads();
+  };
+  if constexpr (STAGES == 3) {
+    for (int jt = 0; jt < n_kv; jt += 3) {
+      step(jt, kb0, vb0, kb2, vb2);
+      if (jt + 1 < n_kv) step(jt + 1, kb1, vb1, kb0, vb0);
+      if (jt + 2 < n_kv) step(jt + 2, kb2, vb2, kb1, vb1);
+    }
+  } else {
+    for (int jt = 0; jt < n_kv; jt += 2) {
+      step(jt, kb0, vb0, kb1, vb1);
+      if (jt + 1 < n_kv) step(jt + 1, kb1, vb1, kb0, vb0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // drain the LDS DMA before exit
+
+  const float l = pair_sum(l_part);
+  const float inv = 1.0f / l;
+  if (my_q < N) {
+    uint16_t* op = o + head + (size_t)my_q * tok;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = f32x4{oacc[dt][4 * g + 0], oacc[dt][4 * g + 1], oacc[dt][4 * g + 2],
+                              oacc[dt][4 * g + 3]} * inv;
+        *(u32x2*)(op + dt * 32 + 8 * g + 4 * hi) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+      }
+    if (hi == 0) lse[((size_t)b * H + hh) * N + my_q] = (m_run + log2f(l)) * kLn2;
+  }
+}
+
+template <int D, int BC, int W, int STAGES, bool CAUSAL>
+hipError_t launch_fwd_dl(const FwdParams& p) {
+  constexpr int BR = W * 32;
+  const int n_qtiles = (p.N + BR - 1) / BR;
+  const long long grid = (long long)p.B * p.H * n_qtiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
+  const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
+  const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((fwd_dl_kernel<D, BC, W, STAGES, CAUSAL>), dim3((unsigned)grid), dim3(W * 64), 0,
+                     p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
+                     (uint16_t*)p.o, p.lse, p.H, p.N, n_qtiles, (int)grid, c, q_and, q_xor);
+  return hipGetLastError();
+}
+
 template <int D, int BC, int WAVES, int OCC, bool CAUSAL, int SCHED = 0>
 hipError_t launch_fwd_t(const FwdParams& p) {
   using C = FwdCfg<D, BC, WAVES>;
@@ -342,12 +618,12 @@ hipError_t launch_fwd_t(const FwdParams& p) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p) {
-  // Tile shapes chosen by measurement on MI355X (K/V tile BC, waves per
-  // workgroup, minimum waves per SIMD); every one is parity-tested.
+  // Direct-to-LDS kernel; tile shapes (K/V tile BC, waves per workgroup,
+  // pipeline stages) chosen by measurement on MI355X, each parity-tested.
   if (p.d == 64) {
-    return p.causal ? launch_fwd_t<64, 64, 4, 2, true>(p) : launch_fwd_t<64, 128, 8, 2, false>(p);
+    return p.causal ? launch_fwd_dl<64, 64, 8, 2, true>(p) : launch_fwd_dl<64, 64, 8, 2, false>(p);
   }
-  return p.causal ? launch_fwd_t<128, 64, 8, 2, true>(p) : launch_fwd_t<128, 64, 8, 2, false>(p);
+  return p.causal ? launch_fwd_dl<128, 64, 4, 2, true>(p) : launch_fwd_dl<128, 64, 8, 2, false>(p);
 }
 
 }  // namespace fa2
