@@ -22,6 +22,7 @@
 //     the lane, so P and dS feed the dV += P^T dO and dK += dS^T Q products
 //     straight from registers; dS also goes to LDS, from which the workgroup
 //     forms its dQ partial = dS K over its 128 keys and adds it atomically.
+#include <limits.h>
 #include <math.h>
 
 #include "fa2_device.hpp"
@@ -330,6 +331,320 @@ __global__ __launch_bounds__(256) void bwd_kernel(
     }
 }
 
+// ---------------------------------------------------------------- B1 ----
+// Direct-to-LDS main kernel.  Every tile lives row-major in LDS, moved there
+// with global_load_lds (no staging VGPRs, no transposing stores); the
+// operands that need the transposed orientation -- Q^T and dO^T for dK and
+// dV, K and dS for dQ -- are read with ds_read_b64_tr_b16 (within each group
+// of 16 lanes, output lane 4a+b receives element b of the 8-byte chunks
+// addressed by lanes a, 4+a, 8+a, 12+a).  Swizzles (XOR on the 16-byte chunk
+// index of row r) keep every access pattern free of bank conflicts:
+//   Q, dO tiles (row reads and transposed reads): 4*(r%4) + (r/4)%4 (d=128),
+//                                                 4*((r/2)%2) + (r/4)%4 (d=64)
+//   K tile (transposed reads only):              4*(r%4) (d=128), 4*((r/2)%2) (d=64)
+//   dS tile [key][query] (8-byte stores, transposed reads):
+//                                                4*((r/2)%2) ^ (r/4)%2 ^ 2*((r/8)%2)
+// None of the transposed-read swizzles depends on row bits above 3, so a
+// fragment's address is a per-lane base (computed once) plus a constant
+// offset per 16-row block -- which keeps the compiler from holding one
+// address register per fragment.
+template <int D>
+struct BwdSwz {
+  __device__ static constexpr int qd(int r) {
+    return D == 128 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
+  }
+  __device__ static constexpr int k(int r) { return D == 128 ? 4 * (r % 4) : 4 * ((r / 2) % 2); }
+  __device__ static constexpr int ds(int r) {
+    return (4 * ((r / 2) % 2)) ^ ((r / 4) % 2) ^ (2 * ((r / 8) % 2));
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Per-lane byte offsets (row block 0, halves u = 0, 1, columns from 0) of a
+// transposed fragment of a row-major, swizzled LDS tile.  Lane l ends up with
+// src[16*blk + 8*(t/4) + 4*(l/32) + t%4][32*cb + l%32] in slot t -- the slot
+// order the accumulator-derived operands use.  None of the swizzles here
+// touches row bits above 3 or chunk bits above 1 for these lanes, so the
+// fragment of 32-column block cb and 16-row block blk sits at
+// (off ^ (cb << 6)) + blk * 16 * ROWBYTES.
+template <int ROWBYTES, typename SWZ>
+__device__ __forceinline__ void tr_offsets(int lane, SWZ swz, uint32_t (&off)[2]) {
+  const int g = lane / 16, i = (lane % 16) / 4, a = lane % 4;
+  const int col = 16 * (g % 2) + 4 * a;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int R = 8 * u + 4 * (g / 2) + i;
+    off[u] = (uint32_t)(R * ROWBYTES + (((col / 8) ^ swz(R)) * 16) + (col % 8) * 2);
+  }
+}
+
+template <int ROWBYTES>
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t* tile, const uint32_t (&off)[2], int cb,
+                                          int blk) {
+  u32x2 part[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint8_t* addr = tile + (off[u] ^ (uint32_t)(cb << 6)) + blk * 16 * ROWBYTES;
+    part[u] = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)addr));
+  }
+  return as_bf16x8(u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
+}
+
+// Hides a value from loop-invariant code motion, so addresses derived from
+// it are formed where they are used instead of being hoisted and held live.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dl_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dq_acc,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int H, int N, int n_ktiles, int grid,
+    float c, float scale) {
+  constexpr int RB = D * 2;                  // bytes per Q / dO / K row
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;             // rows per 1 KB DMA instruction
+  constexpr int QT = kBwdQueries * RB;       // bytes of a Q or dO tile
+  constexpr int KT = kBwdKeys * RB;          // bytes of the K tile
+  constexpr int DSB = kBwdQueries * 2;       // bytes per dS row (64 queries)
+  constexpr int NQI = QT / 1024 / 4;         // Q (and dO) DMA instructions per wave
+  constexpr int NKI = KT / 1024 / 4;         // K DMA instructions per wave
+  static_assert(NQI >= 1 && NKI >= 1, "tile split");
+  using SW = BwdSwz<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t kt_s[KT];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_s0[QT];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_s1[QT];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_s0[QT];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_s1[QT];
+  __shared__ __attribute__((aligned(1024))) uint8_t ds_s[kBwdKeys * DSB];
+  __shared__ __attribute__((aligned(256))) float st_s0[2 * kBwdQueries];  // lse | delta
+  __shared__ __attribute__((aligned(256))) float st_s1[2 * kBwdQueries];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int l32 = lane % 32, hi = lane / 32;
+
+  const int logical = xcd_contiguous_id(blockIdx.x, grid);
+  const int bh = logical / n_ktiles;
+  const int kt_idx = logical % n_ktiles;  // heaviest (first) key tiles first under causal
+  const int b = bh / H, hh = bh % H;
+  const int j0 = kt_idx * kBwdKeys;
+  const int kw0 = j0 + wave * 32;
+  const int my_key = kw0 + l32;
+  const size_t tok = (size_t)H * D;
+  const size_t head = (size_t)b * N * tok + (size_t)hh * D;
+  const size_t rowstat = ((size_t)b * H + hh) * N;
+
+  // K and V rows of this lane's key as B operands
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const size_t off = head + (size_t)min(my_key, N - 1) * tok + hi * 8;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      u32x4 xk = *(const u32x4*)(k + off + cc * 16);
+      u32x4 xv = *(const u32x4*)(v + off + cc * 16);
+      if (my_key >= N) xk = xv = u32x4{0u, 0u, 0u, 0u};
+      kf[cc] = as_bf16x8(xk);
+      vf[cc] = as_bf16x8(xv);
+    }
+  }
+
+  // LDS offsets, computed once per lane.  Q / dO row reads: row t*32 + l%32,
+  // chunk 2*cc + hi at (row_base ^ (cc << 5)) + t * 32 * RB.  dS stores: row
+  // wave*32 + l%32, queries t*32 + 8*g + 4*hi at dsw_base ^ ((4*t + g) << 4).
+  uint32_t row_base = (uint32_t)(l32 * RB + ((hi ^ SW::qd(l32)) * 16));
+  uint32_t trq[2], trk[2], trs[2];
+  tr_offsets<RB>(lane, [](int r) { return SW::qd(r); }, trq);
+  tr_offsets<RB>(lane, [](int r) { return SW::k(r); }, trk);
+  tr_offsets<DSB>(lane, [](int r) { return SW::ds(r); }, trs);
+  uint32_t dsw_base;
+  {
+    const int row = wave * 32 + l32;
+    dsw_base = (uint32_t)(row * DSB + SW::ds(row) * 16 + 8 * hi);
+  }
+
+  // DMA helpers (rows past N repeat row N-1; those rows are masked out).
+  // `ln` is the lane index passed through opaque() so that the per-lane
+  // addresses are formed at each issue instead of being held in registers.
+  auto dma_rows = [&](const uint16_t* src, int n0, uint8_t* dst, int m, int ln, auto swz)
+      __attribute__((always_inline)) {
+    const int r = m * RPI + ln / CPR, slot = ln % CPR;
+    const uint32_t lane_off =
+        (uint32_t)(min(r, N - 1 - n0) * (int)tok + (slot ^ swz(r)) * 8);
+    const uint16_t* g = src + head + (size_t)n0 * tok + lane_off;
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                     (void __attribute__((address_space(3)))*)(dst + m * 1024),
+                                     16, 0, 0);
+  };
+  auto issue_step = [&](int it, uint8_t* qd, uint8_t* dod, float* st)
+      __attribute__((always_inline)) {
+    const int q0 = it * kBwdQueries;
+    const int ln = (int)opaque((uint32_t)lane);
+#pragma unroll
+    for (int u = 0; u < NQI; ++u) {
+      dma_rows(q, q0, qd, wave * NQI + u, ln, [](int r) { return SW::qd(r); });
+      dma_rows(dout, q0, dod, wave * NQI + u, ln, [](int r) { return SW::qd(r); });
+    }
+    if (wave < 2) {
+      const float* src = (wave == 0 ? lse : delta) + rowstat + q0 + min(ln, N - 1 - q0);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)(st + wave * kBwdQueries),
+                                       4, 0, 0);
+    }
+  };
+
+  f32x16 dk_acc[D / 32], dv_acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    dk_acc[dt] = f32x16{};
+    dv_acc[dt] = f32x16{};
+  }
+
+  const int n_qtiles = (N + kBwdQueries - 1) / kBwdQueries;
+  const int it0 = CAUSAL ? j0 / kBwdQueries : 0;
+
+#pragma unroll
+  for (int u = 0; u < NKI; ++u) dma_rows(k, j0, kt_s, wave * NKI + u, lane, [](int r) { return SW::k(r); });
+  if (it0 < n_qtiles) issue_step(it0, q_s0, do_s0, st_s0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  auto step = [&](int it, const uint8_t* qs, const uint8_t* dos, const float* st, uint8_t* qn,
+                  uint8_t* don, float* stn) __attribute__((always_inline)) {
+    const int q0 = it * kBwdQueries;
+    if (it + 1 < n_qtiles) issue_step(it + 1, qn, don, stn);
+    row_base = opaque(row_base);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      trq[u] = opaque(trq[u]);
+      trk[u] = opaque(trk[u]);
+      trs[u] = opaque(trs[u]);
+    }
+    dsw_base = opaque(dsw_base);
+
+    // S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x16{};
+      dp[t] = f32x16{};
+    }
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t off = (row_base ^ (uint32_t)(cc << 5)) + t * 32 * RB;
+        s[t] = mfma32(*(const bf16x8*)(qs + off), kf[cc], s[t]);
+        dp[t] = mfma32(*(const bf16x8*)(dos + off), vf[cc], dp[t]);
+      }
+
+    // P = exp2(S*c - L*log2e), dS = P * (dP - D); masked entries are 0.
+    // Entry (t, g, e) is query q0 + 4*hi + C with C = t*32 + 8*g + e, visible
+    // iff lo <= C < hi_lim: two compares against per-lane bounds.
+    const bool need_mask =
+        (CAUSAL && kw0 + 31 > q0) || (q0 + kBwdQueries > N) || (kw0 + 32 > N);
+    const int lo = CAUSAL ? my_key - q0 - 4 * hi : INT_MIN;
+    const int hi_lim = my_key < N ? N - q0 - 4 * hi : INT_MIN;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = t * 32 + 8 * g + 4 * hi;
+        const f32x4 l4 = *(const f32x4*)(st + qr);
+        const f32x4 d4 = *(const f32x4*)(st + kBwdQueries + qr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const int C = t * 32 + 8 * g + e;
+          float pr = fast_exp2(fmaf(s[t][r], c, -l4[e] * kLog2e));
+          if (need_mask && !(lo <= C && C < hi_lim)) pr = 0.f;
+          s[t][r] = pr;
+          dp[t][r] = pr * (dp[t][r] - d4[e]);
+        }
+      }
+
+    // dV += P^T dO and dK += dS^T Q: B operands dO^T and Q^T read transposed
+#pragma unroll
+    for (int cc = 0; cc < kBwdQueries / 16; ++cc) {
+      const int r0 = 8 * (cc % 2);
+      const f32x16& sv = s[cc / 2];
+      const f32x16& dsv = dp[cc / 2];
+      const bf16x8 pf = to_bf16x8(f32x8{sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
+                                        sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]});
+      const bf16x8 dsf = to_bf16x8(f32x8{dsv[r0], dsv[r0 + 1], dsv[r0 + 2], dsv[r0 + 3],
+                                         dsv[r0 + 4], dsv[r0 + 5], dsv[r0 + 6], dsv[r0 + 7]});
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        dv_acc[dt] = mfma32(pf, tr_frag<RB>(dos, trq, dt, cc), dv_acc[dt]);
+        dk_acc[dt] = mfma32(dsf, tr_frag<RB>(qs, trq, dt, cc), dk_acc[dt]);
+      }
+    }
+
+    // dS (bf16) -> LDS [key][query], 4 consecutive queries per 8-byte store
+    {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const bf16x4 x = to_bf16x4(f32x4{dp[t][4 * g], dp[t][4 * g + 1], dp[t][4 * g + 2],
+                                           dp[t][4 * g + 3]});
+          *(u32x2*)(ds_s + (dsw_base ^ (uint32_t)((4 * t + g) << 4))) = __builtin_bit_cast(u32x2, x);
+        }
+    }
+    __syncthreads();
+
+    // dQ partial = scale * dS K over this workgroup's 128 keys, added atomically
+    constexpr int kTilesPerWave = D / 64;
+#pragma unroll
+    for (int u = 0; u < kTilesPerWave; ++u) {
+      const int tile = wave * kTilesPerWave + u;
+      const int t = tile % 2, dt = tile / 2;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < kBwdKeys / 16; ++cc) {
+        const bf16x8 a = tr_frag<DSB>(ds_s, trs, t, cc);
+        const bf16x8 bk = tr_frag<RB>(kt_s, trk, dt, cc);
+        acc = mfma32(a, bk, acc);
+      }
+      float* dst = dq_acc + head + (size_t)(q0 + t * 32) * tok + dt * 32;
+      const int lane_off = 4 * hi * (int)tok + l32;
+      if (q0 + kBwdQueries <= N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          atomicAdd(dst + (8 * (r / 4) + r % 4) * tok + lane_off, scale * acc[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (q0 + t * 32 + acc_row(r, hi) < N)
+            atomicAdd(dst + (8 * (r / 4) + r % 4) * tok + lane_off, scale * acc[r]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // next step's tiles have landed
+    __syncthreads();
+  };
+  for (int it = it0; it < n_qtiles; it += 2) {
+    step(it, q_s0, do_s0, st_s0, q_s1, do_s1, st_s1);
+    if (it + 1 < n_qtiles) step(it + 1, q_s1, do_s1, st_s1, q_s0, do_s0, st_s0);
+  }
+
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kw0 + acc_row(r, hi);
+      if (key < N) {
+        const size_t off = head + (size_t)key * tok + dt * 32 + l32;
+        dk[off] = to_bf16_bits(scale * dk_acc[dt][r]);
+        dv[off] = to_bf16_bits(dv_acc[dt][r]);
+      }
+    }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdParams& p) {
   const long long rows = (long long)p.B * p.N * p.H;
@@ -346,7 +661,7 @@ hipError_t launch_bwd_t(const BwdParams& p) {
     const int n_ktiles = (p.N + kBwdKeys - 1) / kBwdKeys;
     const long long grid = (long long)p.B * p.H * n_ktiles;
     const float c = (float)((double)p.scale * 1.4426950408889634);
-    hipLaunchKernelGGL((bwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kBwdThreads), 0,
+    hipLaunchKernelGGL((bwd_dl_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kBwdThreads), 0,
                        p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
                        (const uint16_t*)p.v, (const uint16_t*)p.dout, p.lse, p.delta,
                        p.dq_acc, (uint16_t*)p.dk, (uint16_t*)p.dv, p.H, p.N, n_ktiles,
