@@ -12,8 +12,10 @@ on O and L produced by fa2_fwd beforehand.
 
 FLOPs follow the usual convention: 4*B*H*N^2*d per forward, halved if causal;
 a backward pass counts 2.5x its forward.  Timing uses HIP events on the stream
-the kernels are launched on, with an event pair around every launch, so each
-kernel's average duration is measured inside the timed region as well.
+the kernels are launched on.  Inside the timed region the K steps are issued
+grouped by launch (K calls of one kernel back to back, then the next), with an
+event pair around each group, so each kernel's average duration is measured
+there as well.
 
 Prints ONE JSON line.  Besides the throughput it carries:
   roofline      the dominant kernel's achieved TFLOP/s against the bf16 dense
@@ -41,18 +43,24 @@ DEFAULT_PAIR = ("fwd_b8_h16_n1024_d64_full", "fwd_b8_h16_n1024_d64_causal")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def kernel_source_digest() -> str:
-    """Digest of the kernel sources; counter figures are tied to it."""
+KERNEL_SOURCES = {
+    False: ("fa2_device.hpp", "fa2_internal.hpp", "fa2_fwd.hip"),
+    True: ("fa2_device.hpp", "fa2_internal.hpp", "fa2_bwd.hip"),
+}
+
+
+def kernel_source_digest(backward: bool) -> str:
+    """Digest of the sources of the forward (or backward) kernels; counter
+    figures taken on one build are tied to it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_tiled_attention_30_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in KERNEL_SOURCES[backward]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_key: str):
+def load_traffic(kernel_key: str, backward: bool):
     """HBM bytes per launch measured by rocprofv3 for this kernel, if current."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -60,7 +68,7 @@ def load_traffic(kernel_key: str):
     except (OSError, ValueError):
         return None
     entry = data.get(kernel_key)
-    if not entry or entry.get("source_digest") != kernel_source_digest():
+    if not entry or entry.get("source_digest") != kernel_source_digest(backward):
         return None
     return entry.get("bytes_per_launch")
 
@@ -157,18 +165,21 @@ def main():
             fn()
     torch.cuda.synchronize()
 
+    # The K steps are issued grouped by launch: K back-to-back calls of the
+    # first launch, then K of the next.  An event pair brackets each group, so
+    # a kernel's average duration carries no event packets between its calls.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
-          for _ in range(K)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in launches]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for s in range(K):
-        ev[s][0].record(stream)
-        for j, (_, fn, _) in enumerate(launches):
+    for j, (_, fn, _) in enumerate(launches):
+        ev[j][0].record(stream)
+        for _ in range(K):
             fn()
-            ev[s][j + 1].record(stream)
+        ev[j][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
 
@@ -176,8 +187,7 @@ def main():
     ms_per_step = total_ms / K
     step_flops = sum(f for _, _, f in launches)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
-    per_kernel_ms = [float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)]))
-                     for j in range(len(launches))]
+    per_kernel_ms = [a.elapsed_time(b) / K for a, b in ev]
     dom = int(np.argmax(per_kernel_ms))
     dom_name, _, dom_flops = launches[dom]
     achieved = dom_flops / (per_kernel_ms[dom] * 1e-3) / 1e12
@@ -189,7 +199,7 @@ def main():
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": load_traffic(dom_name),
+        "traffic": load_traffic(dom_name, ws[dom].backward),
         "avg_launch_ms": round(per_kernel_ms[dom], 5),
         "flops_per_launch": dom_flops,
     }
