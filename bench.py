@@ -76,8 +76,10 @@ def load_traffic(kernel_key: str, backward: bool):
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=20)
+    # The warm-up is long enough (tens of ms of GPU work at the default
+    # workload) for the GPU clock to settle before the timed region.
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--workload", default=None,
                    help="one workload name (default: the N=1024 d=64 pair)")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")

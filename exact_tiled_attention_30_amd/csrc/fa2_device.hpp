@@ -60,6 +60,20 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, kWave);
 }
 
+// v_max3_f32 / v_max_f32 without the NaN-quieting canonicalisation the
+// compiler wraps around fmaxf in IEEE mode (scores are finite or -inf; a NaN
+// input still propagates through the exp).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // max / sum of a value over the lane pair (l, l ^ 32) with one
 // v_permlane32_swap: its two results are the two halves' values, in some
 // order, in every lane -- the symmetric combinations below do not depend on
@@ -67,7 +81,7 @@ __device__ __forceinline__ float swap_halves(float x) {
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2f(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,

@@ -43,285 +43,6 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int BC, int WAVES>
-struct FwdCfg {
-  static constexpr int kWaves = WAVES;
-  static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kRowsPerWave = 32;
-  static constexpr int BR = kWaves * kRowsPerWave;
-  // LDS row strides (bf16 elements).  K rows are padded by 16 bytes so 8
-  // lanes reading 16 bytes each from 8 consecutive rows hit distinct banks;
-  // V^T rows by 8 bytes so 16 lanes reading 8 bytes from 16 rows do.
-  static constexpr int kKStride = D + 8;
-  static constexpr int kVStride = BC + 4;
-  static constexpr int kKTile = BC * kKStride;
-  static constexpr int kVTile = D * kVStride;
-  // Global -> LDS staging: K in 16-byte chunks; V in units of KPU keys x 8 d
-  // (transposed on the way into LDS).  Threads beyond the work idle.
-  static constexpr int kKChunkCount = BC * D / 8;
-  static constexpr int kKChunks = (kKChunkCount + kThreads - 1) / kThreads;
-  static constexpr int kKeysPerUnit = (BC / 4) * (D / 8) >= kThreads ? 4 : 2;
-  static constexpr int kVUnitCount = (BC / kKeysPerUnit) * (D / 8);
-  static constexpr int kVUnits = (kVUnitCount + kThreads - 1) / kThreads;
-  static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
-};
-
-// Two bf16 from element i of two 8-element rows, packed (row a in the low half).
-__device__ __forceinline__ uint32_t pack_col(const u32x4& a, const u32x4& b, int i) {
-  const uint32_t x = a[i / 2], y = b[i / 2];
-  return (i & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-}
-
-template <int D, int BC, int WAVES, int OCC, bool CAUSAL, int SCHED = 0>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC))) void fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int H, int N, int n_qtiles, int grid, float c, uint32_t q_and, uint32_t q_xor) {
-  using C = FwdCfg<D, BC, WAVES>;
-  constexpr int KPU = C::kKeysPerUnit;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2 * C::kKTile];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2 * C::kVTile];
-
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int l32 = lane % 32, hi = lane / 32;
-
-  // ---- tile scheduler: workgroup -> (batch, head, Q tile)
-  const int logical = xcd_contiguous_id(blockIdx.x, grid);
-  const int bh = logical / n_qtiles;
-  int qt = logical % n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest Q tiles of a head first
-  const int b = bh / H, hh = bh % H;
-  const int q0 = qt * C::BR;
-  const int qw0 = q0 + wave * C::kRowsPerWave;  // first query row of this wave
-  const int my_q = qw0 + l32;                   // the query row this lane owns
-  const size_t tok = (size_t)H * D;             // elements between tokens
-  const size_t head = (size_t)b * N * tok + (size_t)hh * D;
-
-  // ---- Q tile -> B-operand fragments, kept in VGPRs for the whole loop.
-  bf16x8 qf[D / 16];
-  {
-    const uint16_t* qp = q + head + (size_t)my_q * tok + 8 * hi;
-#pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (my_q < N) x = *(const u32x4*)(qp + 16 * cc);
-      // scale < 0: negate Q (exact) and use |scale|; scale == 0: zero Q and
-      // use c = 1, so every visible score is exactly 0 and P exactly 1
-      x = (x & q_and) ^ q_xor;
-      qf[cc] = as_bf16x8(x);
-    }
-  }
-
-  const int kv_len = CAUSAL ? min(N, q0 + C::BR) : N;
-  const int n_kv = (kv_len + BC - 1) / BC;
-
-  // ---- K/V staging through registers into the double-buffered LDS tiles.
-  u32x4 kreg[C::kKChunks];
-  u32x4 vreg[C::kVUnits][KPU];
-  auto load_tile = [&](int jt) __attribute__((always_inline)) {
-    const int kv0 = jt * BC;
-#pragma unroll
-    for (int it = 0; it < C::kKChunks; ++it) {
-      const int ci = tid + it * C::kThreads;
-      const int key = ci / (D / 8), dc = ci % (D / 8);
-      const int gk = kv0 + key;
-      kreg[it] = u32x4{0u, 0u, 0u, 0u};
-      if (ci < C::kKChunkCount && gk < N)
-        kreg[it] = *(const u32x4*)(k + head + (size_t)gk * tok + dc * 8);
-    }
-#pragma unroll
-    for (int it = 0; it < C::kVUnits; ++it) {
-      const int ui = tid + it * C::kThreads;
-      const int kg = ui / (D / 8), dc = ui % (D / 8);
-#pragma unroll
-      for (int kk = 0; kk < KPU; ++kk) {
-        const int gk = kv0 + kg * KPU + kk;
-        vreg[it][kk] = u32x4{0u, 0u, 0u, 0u};
-        if (ui < C::kVUnitCount && gk < N)
-          vreg[it][kk] = *(const u32x4*)(v + head + (size_t)gk * tok + dc * 8);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* kd = ks + buf * C::kKTile;
-#pragma unroll
-    for (int it = 0; it < C::kKChunks; ++it) {
-      const int ci = tid + it * C::kThreads;
-      const int key = ci / (D / 8), dc = ci % (D / 8);
-      if (ci < C::kKChunkCount) *(u32x4*)(kd + key * C::kKStride + dc * 8) = kreg[it];
-    }
-    uint16_t* vd = vt + buf * C::kVTile;
-#pragma unroll
-    for (int it = 0; it < C::kVUnits; ++it) {
-      const int ui = tid + it * C::kThreads;
-      const int kg = ui / (D / 8), dc = ui % (D / 8);
-      if (ui >= C::kVUnitCount) continue;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint16_t* dst = vd + (dc * 8 + i) * C::kVStride + kg * KPU;
-        if constexpr (KPU == 4) {
-          *(u32x2*)dst = u32x2{pack_col(vreg[it][0], vreg[it][1], i),
-                               pack_col(vreg[it][2], vreg[it][3], i)};
-        } else {
-          *(uint32_t*)dst = pack_col(vreg[it][0], vreg[it][1], i);
-        }
-      }
-    }
-  };
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
-  float m_run = -INFINITY;  // reference max of this row, log2 units
-  float l_part = 0.f;       // this lane's share of the row sum, relative to m_run
-
-  if (n_kv > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int jt = 0; jt < n_kv; ++jt) {
-    const int buf = jt & 1;
-    if (jt + 1 < n_kv) load_tile(jt + 1);
-    const int kv0 = jt * BC;
-    const bool wave_active = !CAUSAL || kv0 <= qw0 + C::kRowsPerWave - 1;
-    if (wave_active) {
-      const uint16_t* kb = ks + buf * C::kKTile;
-      const uint16_t* vb = vt + buf * C::kVTile;
-
-      // S^T = K_j Q_i^T (scores of this lane's query against BC keys).  The K
-      // fragments are read kPrefetch MFMAs ahead of their use so LDS latency
-      // hides behind the MFMA pipeline.
-      constexpr int kSteps = (D / 16) * (BC / 32);
-      constexpr int kPrefetch = 4;
-      f32x16 s[BC / 32];
-#pragma unroll
-      for (int kt = 0; kt < BC / 32; ++kt) s[kt] = f32x16{};
-      auto kload = [&](int i) __attribute__((always_inline)) {
-        const int cc = i / (BC / 32), kt = i % (BC / 32);
-        return *(const bf16x8*)(kb + (kt * 32 + l32) * C::kKStride + cc * 16 + hi * 8);
-      };
-      bf16x8 kring[kPrefetch];
-#pragma unroll
-      for (int i = 0; i < kPrefetch; ++i) kring[i] = kload(i);
-#pragma unroll
-      for (int i = 0; i < kSteps; ++i) {
-        const int cc = i / (BC / 32), kt = i % (BC / 32);
-        const bf16x8 a = kring[i % kPrefetch];
-        if (i + kPrefetch < kSteps) kring[i % kPrefetch] = kload(i + kPrefetch);
-        s[kt] = mfma32(a, qf[cc], s[kt]);
-      }
-      if constexpr (SCHED >= 1) {
-        // keep kPrefetch K reads in flight ahead of the MFMA that uses them
-        __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);
-#pragma unroll
-        for (int i = 0; i < kSteps - kPrefetch; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
-      }
-
-      // element mask on diagonal-crossing and ragged tiles only
-      const bool need_mask = (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kt = 0; kt < BC / 32; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kt * 32 + acc_row(r, hi);
-            const bool visible = key < N && (!CAUSAL || key <= my_q);
-            if (!visible) s[kt][r] = -INFINITY;
-          }
-      }
-
-      // online softmax statistics: tile max; the reference moves only when a
-      // row's max rises by more than kRescaleSlack
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < BC / 32; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
-      mx = pair_max(mx);
-      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-      if (wave_any(mt > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-        l_part *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-        m_run = m_new;
-      }
-      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-
-      // P = exp2(S*c - m) and O^T += V_j^T P^T.  P for key chunk cc+1 is
-      // formed while the MFMAs of chunk cc run.  Contraction slot t of lane
-      // half hi pairs with key 16*cc + 8*(t/4) + 4*hi + t%4 in both operands.
-      float rs = 0.f;
-      auto chunk_p = [&](int cc) __attribute__((always_inline)) {
-        // c > 0, so a masked score of -inf gives exp2(-inf) = 0
-        const f32x16& sv = s[cc / 2];
-        const int r0 = 8 * (cc % 2);
-        f32x8 pv;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          pv[t] = fast_exp2(fmaf(sv[r0 + t], c, -mref));
-          rs += pv[t];
-        }
-        return to_bf16x8(pv);
-      };
-      bf16x8 pf = chunk_p(0);
-#pragma unroll
-      for (int cc = 0; cc < BC / 16; ++cc) {
-        u32x4 vfrag[D / 32];
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const uint16_t* vr = vb + (dt * 32 + l32) * C::kVStride + cc * 16 + 4 * hi;
-          const u32x2 lo = *(const u32x2*)vr;
-          const u32x2 up = *(const u32x2*)(vr + 8);
-          vfrag[dt] = u32x4{lo[0], lo[1], up[0], up[1]};
-        }
-        const bf16x8 pcur = pf;
-        if (cc + 1 < BC / 16) pf = chunk_p(cc + 1);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          oacc[dt] = mfma32(as_bf16x8(vfrag[dt]), pcur, oacc[dt]);
-        if constexpr (SCHED >= 2) {
-          // this chunk's V reads first, then each MFMA followed by a slice of
-          // the next chunk's softmax VALU work
-          __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 1);
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x002, 28 / (D / 32), 1);
-          }
-        }
-      }
-      l_part += rs;
-    }
-    if (jt + 1 < n_kv) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: one division by l per row, bf16 O, natural-log L
-  const float l = pair_sum(l_part);
-  const float inv = 1.0f / l;
-  if (my_q < N) {
-    uint16_t* op = o + head + (size_t)my_q * tok;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 x = f32x4{oacc[dt][4 * g + 0], oacc[dt][4 * g + 1], oacc[dt][4 * g + 2],
-                              oacc[dt][4 * g + 3]} * inv;
-        *(u32x2*)(op + dt * 32 + 8 * g + 4 * hi) = __builtin_bit_cast(u32x2, to_bf16x4(x));
-      }
-    if (hi == 0) lse[((size_t)b * H + hh) * N + my_q] = (m_run + log2f(l)) * kLn2;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Direct-to-LDS variant (the production forward kernel).
 //
@@ -372,34 +93,20 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   __shared__ __attribute__((aligned(1024))) uint8_t vb2[STAGES > 2 ? TILE : 16];
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int l32 = lane % 32, hi = lane / 32;
 
+  // Work item: non-causal, one Q tile; causal, the pair (n_qtiles-1-p, p)
+  // of a heavy and a light Q tile, so every workgroup streams the same
+  // number of K/V tiles (n_qtiles + 1 tile rows of keys) whatever p is.
   const int logical = xcd_contiguous_id(blockIdx.x, grid);
-  const int bh = logical / n_qtiles;
-  int qt = logical % n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  const int per_head = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+  const int bh = logical / per_head;
+  const int item = logical % per_head;
+  const int n_pass = (CAUSAL && item != n_qtiles - 1 - item) ? 2 : 1;
   const int b = bh / H, hh = bh % H;
-  const int q0 = qt * BR;
-  const int qw0 = q0 + wave * 32;
-  const int my_q = qw0 + l32;
   const size_t tok = (size_t)H * D;
   const size_t head = (size_t)b * N * tok + (size_t)hh * D;
-
-  bf16x8 qf[D / 16];
-  {
-    const uint16_t* qp = q + head + (size_t)min(my_q, N - 1) * tok + 8 * hi;
-#pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) {
-      u32x4 x = *(const u32x4*)(qp + 16 * cc);
-      if (my_q >= N) x = u32x4{0u, 0u, 0u, 0u};
-      x = (x & q_and) ^ q_xor;
-      qf[cc] = as_bf16x8(x);
-    }
-  }
-
-  const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
-  const int n_kv = (kv_len + BC - 1) / BC;
 
   // Per-lane byte offsets of the chunks this lane deposits, relative to the
   // tile's first key row; the tile base is a scalar pointer.
@@ -436,6 +143,27 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
           (void __attribute__((address_space(3)))*)(vd + m * 1024), 16, 0, 0);
     }
   };
+
+  for (int pass = 0; pass < n_pass; ++pass) {
+  const int qt = CAUSAL ? (pass == 0 ? n_qtiles - 1 - item : item) : item;
+  const int q0 = qt * BR;
+  const int qw0 = q0 + wave * 32;
+  const int my_q = qw0 + l32;
+
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qp = q + head + (size_t)min(my_q, N - 1) * tok + 8 * hi;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      u32x4 x = *(const u32x4*)(qp + 16 * cc);
+      if (my_q >= N) x = u32x4{0u, 0u, 0u, 0u};
+      x = (x & q_and) ^ q_xor;
+      qf[cc] = as_bf16x8(x);
+    }
+  }
+
+  const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_kv = (kv_len + BC - 1) / BC;
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -479,11 +207,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
           if (!visible) s[kt][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    float mx = max2f(s[0][0], s[0][1]);
 #pragma unroll
-    for (int kt = 0; kt < BC / 32; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
+    for (int i = 2; i < BC / 2; i += 2) mx = max3f(mx, s[i / 16][i % 16], s[i / 16][i % 16 + 1]);
     mx = pair_max(mx);
     const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
     if (wave_any(mt > m_run + kRescaleSlack)) {
@@ -579,13 +305,15 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
       }
     if (hi == 0) lse[((size_t)b * H + hh) * N + my_q] = (m_run + log2f(l)) * kLn2;
   }
+  if (pass + 1 < n_pass) __syncthreads();  // every wave is done with the LDS tiles
+  }
 }
 
 template <int D, int BC, int W, int STAGES, bool CAUSAL>
 hipError_t launch_fwd_dl(const FwdParams& p) {
   constexpr int BR = W * 32;
   const int n_qtiles = (p.N + BR - 1) / BR;
-  const long long grid = (long long)p.B * p.H * n_qtiles;
+  const long long grid = (long long)p.B * p.H * (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
@@ -598,32 +326,22 @@ hipError_t launch_fwd_dl(const FwdParams& p) {
   return hipGetLastError();
 }
 
-template <int D, int BC, int WAVES, int OCC, bool CAUSAL, int SCHED = 0>
-hipError_t launch_fwd_t(const FwdParams& p) {
-  using C = FwdCfg<D, BC, WAVES>;
-  const int n_qtiles = (p.N + C::BR - 1) / C::BR;
-  const long long grid = (long long)p.B * p.H * n_qtiles;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
-  const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
-  const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
-  (void)hipGetLastError();
-  hipLaunchKernelGGL((fwd_kernel<D, BC, WAVES, OCC, CAUSAL, SCHED>), dim3((unsigned)grid), dim3(C::kThreads), 0,
-                     p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
-                     (uint16_t*)p.o, p.lse, p.H, p.N, n_qtiles, (int)grid, c, q_and, q_xor);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p) {
-  // Direct-to-LDS kernel; tile shapes (K/V tile BC, waves per workgroup,
-  // pipeline stages) chosen by measurement on MI355X, each parity-tested.
-  if (p.d == 64) {
-    return p.causal ? launch_fwd_dl<64, 64, 8, 2, true>(p) : launch_fwd_dl<64, 64, 8, 2, false>(p);
+  // Tile shapes (K/V tile 64 keys; 8 waves = 256-row Q tiles, or 4 waves =
+  // 128 rows) chosen by measurement on MI355X, each parity-tested.  Causal
+  // grids of fewer than two 8-wave workgroups per CU use the 4-wave tiles.
+  constexpr int kCus = 256;
+  if (!p.causal) {
+    return p.d == 64 ? launch_fwd_dl<64, 64, 8, 2, false>(p) : launch_fwd_dl<128, 64, 8, 2, false>(p);
   }
-  return p.causal ? launch_fwd_dl<128, 64, 4, 2, true>(p) : launch_fwd_dl<128, 64, 8, 2, false>(p);
+  const long long pairs8 = (long long)p.B * p.H * (((p.N + 255) / 256 + 1) / 2);
+  const bool small = pairs8 < 2 * kCus;
+  if (p.d == 64) {
+    return small ? launch_fwd_dl<64, 64, 4, 2, true>(p) : launch_fwd_dl<64, 64, 8, 2, true>(p);
+  }
+  return small ? launch_fwd_dl<128, 64, 4, 2, true>(p) : launch_fwd_dl<128, 64, 8, 2, true>(p);
 }
 
 }  // namespace fa2

@@ -133,3 +133,25 @@ def test_full_size_workloads_sampled_rows(w):
     rep = forward_report(o_got, lse_got, o_ref, lse_ref)
     print(f"  {rep}", flush=True)
     assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_wide_grid_ragged(d):
+    # Enough heads that the causal grid takes 256-row Q tiles, each workgroup
+    # running a heavy and a light tile (or the middle tile alone); N ragged.
+    B, H, N = 2, 128, 600
+    print(f"[fwd causal wide] B={B} H={H} N={N} d={d}", flush=True)
+    x = make_inputs(B, H, N, d, seed=13)
+    d_ = _dev(x)
+    o = torch.empty_like(d_["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    binding.fa2_fwd(d_["q"], d_["k"], d_["v"], o, lse, True, d ** -0.5)
+    torch.cuda.synchronize()
+    del d_
+    every = [(b, h, i) for (b, h) in ((0, 0), (1, 127)) for i in range(N)]
+    rows = np.concatenate([np.array(every, dtype=np.int64), sample_rows(B, H, N, seed=3)])
+    o_ref, lse_ref = oracle.attention_forward_rows(x["q"], x["k"], x["v"], True, d ** -0.5, rows)
+    b, h, i = (torch.as_tensor(rows[:, c], device="cuda") for c in range(3))
+    rep = forward_report(o[b, i, h].cpu(), lse[b, h, i].cpu(), o_ref, lse_ref)
+    print(f"  {rep}", flush=True)
+    assert rep["ok"], rep
