@@ -12,16 +12,17 @@
 // gradient): dV = P^T dO, dP = dO V^T, dS = P * (dP - D), dK = scale dS^T Q,
 // dQ = scale dS K.
 //
-// gfx950 mapping of the main kernel (bwd_kernel):
+// gfx950 mapping of the main kernel (bwd_dl_kernel):
 //   * workgroup = 4 waves = 128 keys of one (batch, head); each wave owns 32
 //     keys and keeps their K and V rows in VGPRs (MFMA B operands) and their
 //     dK, dV accumulators in registers for the whole loop;
-//   * it walks 64-query tiles of Q and dO, staged in LDS in both row-major and
-//     transposed form (the MFMA operand orientations need both);
-//   * S = Q K^T and dP = dO V^T put the key on the accumulator column, i.e. on
-//     the lane, so P and dS feed the dV += P^T dO and dK += dS^T Q products
-//     straight from registers; dS also goes to LDS, from which the workgroup
-//     forms its dQ partial = dS K over its 128 keys and adds it atomically.
+//   * it walks 64-query steps of Q, dO and the L / D rows, moved global ->
+//     LDS by DMA one step ahead into a second buffer;
+//   * S = K Q^T and dP = V dO^T put the key on the lane, so P and dS feed the
+//     dV += P dO and dK += dS Q products straight from registers (as A
+//     operands), with dO^T and Q^T read transposed from the same row-major
+//     LDS tiles; dS also goes to LDS, from which the workgroup forms its dQ
+//     partial = dS K over its 128 keys and adds it atomically.
 #include <limits.h>
 #include <math.h>
 
@@ -92,243 +93,6 @@ __global__ __launch_bounds__(256) void bwd_convert_dq_kernel(const float* __rest
   const f32x4 b = *(const f32x4*)(dq_acc + 8 * i + 4);
   const bf16x8 r = to_bf16x8(f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
   *(u32x4*)(dq + 8 * i) = as_u32x4(r);
-}
-
-// ---------------------------------------------------------------- B1 ----
-template <int D>
-struct BwdCfg {
-  static constexpr int kQStride = D + 8;                 // row-major Q / dO tiles
-  static constexpr int kQTStride = kBwdQueries + 4;      // transposed Q / dO tiles
-  static constexpr int kSStride = kBwdKeys + 8;          // dS tile [query][key]
-  static constexpr int kKTStride = kBwdKeys + 8;         // K^T [d][key]
-  static constexpr int kRowsPerUnit = D / 32;            // Q rows per staging unit
-  static constexpr int kKeysPerUnit = D / 16;            // keys per K^T staging unit
-  static constexpr int kDqTilesPerWave = D / 64;         // 32x32 dQ tiles per wave
-  static_assert((kBwdQueries / kRowsPerUnit) * (D / 8) == kBwdThreads, "Q staging");
-  static_assert((kBwdKeys / kKeysPerUnit) * (D / 8) == kBwdThreads, "K^T staging");
-};
-
-template <int D>
-struct BwdSmem {
-  using C = BwdCfg<D>;
-  uint16_t qs[kBwdQueries * C::kQStride];
-  uint16_t dos[kBwdQueries * C::kQStride];
-  uint16_t qt[D * C::kQTStride];
-  uint16_t dot[D * C::kQTStride];
-  uint16_t dss[kBwdQueries * C::kSStride];
-  uint16_t kt[D * C::kKTStride];
-  float lse2[kBwdQueries];
-  float dl[kBwdQueries];
-};
-
-// Two bf16 from element i of two 8-element rows, packed (row a low half).
-__device__ __forceinline__ uint32_t pack_pair(const u32x4& a, const u32x4& b, int i) {
-  const uint32_t x = a[i / 2], y = b[i / 2];
-  return (i & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-}
-
-// Stage rows [r0, r0 + KPU) x [8*dc, 8*dc + 8) of a [B,N,H,D] tensor slice:
-// row-major into `rm` (unless null) and transposed into `tr`.
-template <int D, int KPU>
-__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, size_t head,
-                                           size_t tok, int n0, int N, int r0, int dc,
-                                           uint16_t* rm, int rm_stride, uint16_t* tr,
-                                           int tr_stride) {
-  u32x4 x[KPU];
-#pragma unroll
-  for (int kk = 0; kk < KPU; ++kk) {
-    const int n = n0 + r0 + kk;
-    x[kk] = u32x4{0u, 0u, 0u, 0u};
-    if (n < N) x[kk] = *(const u32x4*)(src + head + (size_t)n * tok + dc * 8);
-    if (rm) *(u32x4*)(rm + (r0 + kk) * rm_stride + dc * 8) = x[kk];
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint16_t* dst = tr + (dc * 8 + i) * tr_stride + r0;
-#pragma unroll
-    for (int kk = 0; kk < KPU; kk += 2) *(uint32_t*)(dst + kk) = pack_pair(x[kk], x[kk + 1], i);
-  }
-}
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dq_acc,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int H, int N, int n_ktiles, int grid,
-    float c, float scale) {
-  using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) BwdSmem<D> sm;
-
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int l32 = lane % 32, hi = lane / 32;
-
-  const int logical = xcd_contiguous_id(blockIdx.x, grid);
-  const int bh = logical / n_ktiles;
-  const int kt_idx = logical % n_ktiles;  // heaviest (first) key tiles first under causal
-  const int b = bh / H, hh = bh % H;
-  const int j0 = kt_idx * kBwdKeys;
-  const int kw0 = j0 + wave * 32;  // first key of this wave
-  const int my_key = kw0 + l32;    // the key this lane's accumulator column holds
-  const size_t tok = (size_t)H * D;
-  const size_t head = (size_t)b * N * tok + (size_t)hh * D;
-  const size_t rowstat = ((size_t)b * H + hh) * N;
-
-  // K and V rows of this lane's key: B operands (column = key, 8 d per slot group)
-  bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) {
-    u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-    if (my_key < N) {
-      xk = *(const u32x4*)(k + head + (size_t)my_key * tok + cc * 16 + hi * 8);
-      xv = *(const u32x4*)(v + head + (size_t)my_key * tok + cc * 16 + hi * 8);
-    }
-    kf[cc] = as_bf16x8(xk);
-    vf[cc] = as_bf16x8(xv);
-  }
-  // K^T of the workgroup's 128 keys, for dQ = dS K
-  {
-    constexpr int KPU = C::kKeysPerUnit;
-    const int r0 = (tid / (D / 8)) * KPU, dc = tid % (D / 8);
-    stage_rows<D, KPU>(k, head, tok, j0, N, r0, dc, nullptr, 0, sm.kt, C::kKTStride);
-  }
-
-  f32x16 dk_acc[D / 32], dv_acc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    dk_acc[dt] = f32x16{};
-    dv_acc[dt] = f32x16{};
-  }
-
-  const int n_qtiles = (N + kBwdQueries - 1) / kBwdQueries;
-  const int it0 = CAUSAL ? j0 / kBwdQueries : 0;
-  for (int it = it0; it < n_qtiles; ++it) {
-    const int q0 = it * kBwdQueries;
-    // ---- stage Q, dO (row-major + transposed), L*log2e and D
-    {
-      constexpr int KPU = C::kRowsPerUnit;
-      const int r0 = (tid / (D / 8)) * KPU, dc = tid % (D / 8);
-      stage_rows<D, KPU>(q, head, tok, q0, N, r0, dc, sm.qs, C::kQStride, sm.qt, C::kQTStride);
-      stage_rows<D, KPU>(dout, head, tok, q0, N, r0, dc, sm.dos, C::kQStride, sm.dot,
-                         C::kQTStride);
-      if (tid < kBwdQueries) {
-        const int qi = q0 + tid;
-        sm.lse2[tid] = qi < N ? lse[rowstat + qi] * kLog2e : 0.f;
-        sm.dl[tid] = qi < N ? delta[rowstat + qi] : 0.f;
-      }
-    }
-    __syncthreads();
-
-    // ---- S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = f32x16{};
-      dp[t] = f32x16{};
-    }
-#pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 aq = *(const bf16x8*)(sm.qs + (t * 32 + l32) * C::kQStride + cc * 16 + hi * 8);
-        const bf16x8 ad = *(const bf16x8*)(sm.dos + (t * 32 + l32) * C::kQStride + cc * 16 + hi * 8);
-        s[t] = mfma32(aq, kf[cc], s[t]);
-        dp[t] = mfma32(ad, vf[cc], dp[t]);
-      }
-    }
-
-    // ---- P = exp2(S*c - L*log2e), dS = P * (dP - D); masked entries are 0
-    const bool need_mask = (CAUSAL && kw0 + 31 > q0) || (q0 + kBwdQueries > N) || (kw0 + 32 > N);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qr = t * 32 + 8 * g + 4 * hi;  // local query of register 4*g
-        const f32x4 l4 = *(const f32x4*)(sm.lse2 + qr);
-        const f32x4 d4 = *(const f32x4*)(sm.dl + qr);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = fast_exp2(fmaf(s[t][r], c, -l4[e]));
-          if (need_mask) {
-            const int query = q0 + qr + e;
-            const bool visible = query < N && my_key < N && (!CAUSAL || my_key <= query);
-            if (!visible) p = 0.f;
-          }
-          s[t][r] = p;
-          dp[t][r] = p * (dp[t][r] - d4[e]);
-        }
-      }
-    }
-
-    // ---- dV += P^T dO and dK += dS^T Q (contraction over the 64 queries).
-    // Slot t of lane half hi pairs with query 16*cc + 8*(t/4) + 4*hi + t%4.
-#pragma unroll
-    for (int cc = 0; cc < kBwdQueries / 16; ++cc) {
-      const int r0 = 8 * (cc % 2);
-      const f32x16& sv = s[cc / 2];
-      const f32x16& dsv = dp[cc / 2];
-      const bf16x8 pf = to_bf16x8(f32x8{sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
-                                        sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]});
-      const bf16x8 dsf = to_bf16x8(f32x8{dsv[r0], dsv[r0 + 1], dsv[r0 + 2], dsv[r0 + 3],
-                                         dsv[r0 + 4], dsv[r0 + 5], dsv[r0 + 6], dsv[r0 + 7]});
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const uint16_t* dr = sm.dot + (dt * 32 + l32) * C::kQTStride + cc * 16 + 4 * hi;
-        const u32x2 dlo = *(const u32x2*)dr, dup = *(const u32x2*)(dr + 8);
-        dv_acc[dt] = mfma32(pf, as_bf16x8(u32x4{dlo[0], dlo[1], dup[0], dup[1]}), dv_acc[dt]);
-        const uint16_t* qr = sm.qt + (dt * 32 + l32) * C::kQTStride + cc * 16 + 4 * hi;
-        const u32x2 qlo = *(const u32x2*)qr, qup = *(const u32x2*)(qr + 8);
-        dk_acc[dt] = mfma32(dsf, as_bf16x8(u32x4{qlo[0], qlo[1], qup[0], qup[1]}), dk_acc[dt]);
-      }
-    }
-
-    // ---- dS (bf16) -> LDS [query][key] for the dQ product
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = t * 32 + acc_row(r, hi);
-        sm.dss[ql * C::kSStride + wave * 32 + l32] = to_bf16_bits(dp[t][r]);
-      }
-    __syncthreads();
-
-    // ---- dQ partial = scale * dS K over this workgroup's keys, added atomically
-#pragma unroll
-    for (int u = 0; u < C::kDqTilesPerWave; ++u) {
-      const int tile = wave * C::kDqTilesPerWave + u;  // 0 .. 2*D/32-1
-      const int t = tile % 2, dt = tile / 2;
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int cc = 0; cc < kBwdKeys / 16; ++cc) {
-        const bf16x8 a = *(const bf16x8*)(sm.dss + (t * 32 + l32) * C::kSStride + cc * 16 + hi * 8);
-        const bf16x8 bk = *(const bf16x8*)(sm.kt + (dt * 32 + l32) * C::kKTStride + cc * 16 + hi * 8);
-        acc = mfma32(a, bk, acc);
-      }
-      // accumulator: column = d (lane), rows = queries
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int query = q0 + t * 32 + acc_row(r, hi);
-        if (query < N)
-          atomicAdd(dq_acc + head + (size_t)query * tok + dt * 32 + l32, scale * acc[r]);
-      }
-    }
-    __syncthreads();  // LDS tiles are rewritten by the next step
-  }
-
-  // ---- dK = scale * acc, dV = acc; accumulator column = d (lane), rows = keys
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kw0 + acc_row(r, hi);
-      if (key < N) {
-        const size_t off = head + (size_t)key * tok + dt * 32 + l32;
-        dk[off] = to_bf16_bits(scale * dk_acc[dt][r]);
-        dv[off] = to_bf16_bits(dv_acc[dt][r]);
-      }
-    }
 }
 
 // ---------------------------------------------------------------- B1 ----

@@ -6,22 +6,21 @@
 // causal block skipping of section 5.3 and the split-Q warp partition of
 // section 4.2.  Design for CDNA4, not a port of the A100 kernel:
 //
-//  * One workgroup = one 128-row Q tile of one (batch, head); 4 waves of 64
-//    lanes, each wave owns 32 query rows and its softmax rows outright (no
-//    cross-wave merge).  Grid = B * H * ceil(N / 128), renumbered so each XCD
-//    runs contiguous Q tiles of the same heads (shared K/V in its L2); causal
-//    grids run the heaviest (last) Q tiles of a head first.
+//  * A workgroup of W waves (64 lanes) owns a Q tile of 32*W rows of one
+//    (batch, head); each wave owns 32 query rows and their softmax rows
+//    outright (no cross-wave merge).  Causal workgroups take a heavy and a
+//    light Q tile in turn so all stream the same number of K/V tiles.  Work
+//    items are renumbered so each XCD runs contiguous Q tiles of the same
+//    heads (shared K/V in its L2).
 //  * Both products run on v_mfma_f32_32x32x16_bf16 in transposed form:
 //    S^T = K Q^T (A = K rows from LDS, B = Q held in VGPRs for the whole
-//    loop) and O^T = V^T P^T (A = V^T from LDS, B = P^T straight from the
-//    S^T accumulators after an in-register bf16 conversion).  In both, the
-//    accumulator column -- one query -- is fixed per lane, so row max, row sum,
-//    rescale and the final 1/l are per-lane scalars plus one exchange between
-//    the two lane halves.
-//  * K/V tiles are double-buffered in LDS: the next tile's global loads are
-//    issued (128-bit, coalesced) before the current tile's math and written to
-//    the other buffer afterwards; one barrier per tile.  V is transposed on the
-//    way into LDS so the PV operand reads are contiguous 64-bit loads.
+//    loop) and O^T = V^T P^T (A = V^T read transposed from LDS, B = P^T
+//    straight from the S^T accumulators after an in-register bf16
+//    conversion).  In both, the accumulator column -- one query -- is fixed
+//    per lane, so row max, row sum, rescale and the final 1/l are per-lane
+//    scalars plus one exchange between the two lane halves.
+//  * K/V tiles move global -> LDS by DMA (global_load_lds), double-buffered,
+//    one barrier per tile; see the kernel's comment for the LDS layout.
 //  * Softmax in base 2: t = s * scale*log2(e) in fp32 on the MFMA output
 //    (never folded into bf16 Q), P = exp2(t - m).  l is summed from the fp32
 //    P before the bf16 conversion.  The reference max m is only moved when a
@@ -29,7 +28,7 @@
 //    O rescale (a multiply of every accumulator) is skipped on most tiles; the
 //    stored O/l and L = ln2 * (m + log2 l) are mathematically unchanged, and
 //    P stays <= 2^kRescaleSlack, far from fp32/bf16 overflow.
-//  * Causal: K/V tiles past the Q tile's last row are never visited; a wave
+//  * Causal: K/V tiles past the Q tile's last row are never loaded; a wave
 //    skips tiles entirely above its rows; only tiles crossing the diagonal (or
 //    the ragged end of the sequence) run the element mask.
 #include <math.h>
@@ -44,8 +43,6 @@ namespace {
 constexpr float kRescaleSlack = 8.0f;
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant (the production forward kernel).
-//
 // K and V tiles move HBM/L2 -> LDS with global_load_lds_dwordx4: lane L of a
 // wave deposits its 16 bytes at LDS base + 16*L, so no VGPRs, no ds_write and
 // no VALU packing are spent on staging.  Rows are stored unpadded (D*2 bytes)
