@@ -83,6 +83,9 @@ def parse_args():
     p.add_argument("--workload", default=None,
                    help="one workload name (default: the N=1024 d=64 pair)")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    p.add_argument("--bwd-dq", choices=("two-pass", "atomic"), default="two-pass",
+                   help="dQ strategy of a backward workload: fa2_bwd (a Q-outer dQ pass) "
+                        "or fa2_bwd_atomic_dq (fp32 atomics)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -154,12 +157,16 @@ def main():
         else:
             binding.fa2_fwd(x["q"], x["k"], x["v"], o, lse, w.causal, w.scale)
             dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
-            wsp = torch.empty(binding.fa2_bwd_workspace_bytes(w.B, w.H, w.N, w.d, w.causal),
-                              dtype=torch.uint8, device=dev)
+            atomic = args.bwd_dq == "atomic"
+            sizer = (binding.fa2_bwd_atomic_dq_workspace_bytes if atomic
+                     else binding.fa2_bwd_workspace_bytes)
+            call = binding.fa2_bwd_atomic_dq if atomic else binding.fa2_bwd
+            wsp = torch.empty(sizer(w.B, w.H, w.N, w.d, w.causal), dtype=torch.uint8,
+                              device=dev)
 
-            def bwd(w=w, dq=dq, dk=dk, dv=dv, wsp=wsp):
-                binding.fa2_bwd(x["q"], x["k"], x["v"], o, lse, x["dout"], dq, dk, dv, wsp,
-                                w.causal, w.scale)
+            def bwd(w=w, dq=dq, dk=dk, dv=dv, wsp=wsp, call=call):
+                call(x["q"], x["k"], x["v"], o, lse, x["dout"], dq, dk, dv, wsp, w.causal,
+                     w.scale)
             launches.append((w.name, bwd, w.flops()))
 
     for _ in range(args.warmup):
@@ -226,6 +233,7 @@ def main():
             "B": base.B, "H": base.H, "N": base.N, "d": base.d,
             "causal": [w.causal for w in ws],
             "backward": [w.backward for w in ws],
+            **({"bwd_dq": args.bwd_dq} if any(w.backward for w in ws) else {}),
             "layout": "[B,N,H,d] bf16 in/out, fp32 lse [B,H,N]",
             "parallelism": "single GPU",
         },

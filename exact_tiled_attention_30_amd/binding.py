@@ -6,7 +6,7 @@ stream, and turns status codes into exceptions.  There is no fallback: if the
 library is missing the call fails loudly.
 
 Names mirror include/fa2.h: fa2_fwd, fa2_bwd, fa2_bwd_workspace_bytes,
-fa2_status_string.
+fa2_bwd_atomic_dq, fa2_bwd_atomic_dq_workspace_bytes, fa2_status_string.
 """
 from __future__ import annotations
 
@@ -48,6 +48,10 @@ def lib():
     L.fa2_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                           _i, _i, _i, _i, _i, ctypes.c_float, _vp]
     L.fa2_bwd.restype = _i
+    L.fa2_bwd_atomic_dq_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+    L.fa2_bwd_atomic_dq_workspace_bytes.restype = ctypes.c_size_t
+    L.fa2_bwd_atomic_dq.argtypes = L.fa2_bwd.argtypes
+    L.fa2_bwd_atomic_dq.restype = _i
     L.fa2_status_string.argtypes = [_i]
     L.fa2_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -116,10 +120,11 @@ def fa2_bwd_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int
     return int(lib().fa2_bwd_workspace_bytes(B, H, N, d, int(bool(causal))))
 
 
-def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool, scale: float,
-            stream=None) -> None:
-    """Enqueue the backward pass. workspace: a uint8 device tensor of at least
-    fa2_bwd_workspace_bytes(...) bytes.  Raises Fa2Error."""
+def fa2_bwd_atomic_dq_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    return int(lib().fa2_bwd_atomic_dq_workspace_bytes(B, H, N, d, int(bool(causal))))
+
+
+def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, scale, stream):
     import torch
 
     B, N, H, d = _bnhd(q)
@@ -130,9 +135,25 @@ def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool, scale: f
             raise ValueError(f"{name} must have shape {(B, N, H, d)}")
     _require(lse, torch.float32, "lse")
     _require(workspace, torch.uint8, "workspace")
-    _check(lib().fa2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, H, N, d,
-                         int(bool(causal)), float(scale), _stream(q, stream)))
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), workspace.numel(), B, H, N, d, int(bool(causal)),
+            float(scale), _stream(q, stream))
+
+
+def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool, scale: float,
+            stream=None) -> None:
+    """Enqueue the backward pass (dQ from a Q-outer pass). workspace: a uint8
+    device tensor of at least fa2_bwd_workspace_bytes(...) bytes.  Raises Fa2Error."""
+    _check(lib().fa2_bwd(*_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, scale,
+                                     stream)))
+
+
+def fa2_bwd_atomic_dq(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool, scale: float,
+                      stream=None) -> None:
+    """Enqueue the backward pass with dQ summed by fp32 atomics. workspace: at
+    least fa2_bwd_atomic_dq_workspace_bytes(...) bytes.  Raises Fa2Error."""
+    _check(lib().fa2_bwd_atomic_dq(*_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal,
+                                               scale, stream)))
 
 
 # ---- conveniences that allocate the outputs with torch, then call the above
@@ -151,15 +172,17 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None)
 
 
 def attention_backward(q, k, v, o, lse, dout, causal: bool = False,
-                       scale: float | None = None):
-    """Allocate dQ, dK, dV and the workspace, run fa2_bwd, return (dq, dk, dv)."""
+                       scale: float | None = None, atomic_dq: bool = False):
+    """Allocate dQ, dK, dV and the workspace, run fa2_bwd (or fa2_bwd_atomic_dq),
+    return (dq, dk, dv)."""
     import torch
 
     B, N, H, d = _bnhd(q)
     if scale is None:
         scale = d ** -0.5
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(max(1, fa2_bwd_workspace_bytes(B, H, N, d, causal)), dtype=torch.uint8,
-                     device=q.device)
-    fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, causal, scale)
+    sizer = fa2_bwd_atomic_dq_workspace_bytes if atomic_dq else fa2_bwd_workspace_bytes
+    ws = torch.empty(max(1, sizer(B, H, N, d, causal)), dtype=torch.uint8, device=q.device)
+    (fa2_bwd_atomic_dq if atomic_dq else fa2_bwd)(q, k, v, o, lse, dout, dq, dk, dv, ws, causal,
+                                                 scale)
     return dq, dk, dv

@@ -98,20 +98,33 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d, int causal) {
   (void)causal;
   size_t elems = 0, rows = 0;
   if (check_shape(B, H, N, d, 1.0f, &elems, &rows) != FA2_OK || elems == 0) return 0;
+  return fa2::bwd_delta_bytes(B, H, N);
+}
+
+size_t fa2_bwd_atomic_dq_workspace_bytes(int B, int H, int N, int d, int causal) {
+  (void)causal;
+  size_t elems = 0, rows = 0;
+  if (check_shape(B, H, N, d, 1.0f, &elems, &rows) != FA2_OK || elems == 0) return 0;
   return fa2::bwd_delta_bytes(B, H, N) + fa2::bwd_dq_acc_bytes(B, H, N, d);
 }
 
-int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-            const void* dout, void* dq, void* dk, void* dv, void* workspace,
-            size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
-            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks and launch of the two backward entry points.
+int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
+               void* stream, bool atomic_dq) {
   size_t elems = 0, rows = 0;
   const int st = check_shape(B, H, N, d, scale, &elems, &rows);
   if (st != FA2_OK) return st;
   if (elems == 0) return FA2_OK;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA2_ERR_NULLPTR;
-  if (!workspace || workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d, causal))
-    return FA2_ERR_WORKSPACE;
+  const size_t need = atomic_dq ? fa2_bwd_atomic_dq_workspace_bytes(B, H, N, d, causal)
+                                : fa2_bwd_workspace_bytes(B, H, N, d, causal);
+  if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4) || !aligned(workspace, 16))
@@ -130,9 +143,30 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
 
   char* ws = (char*)workspace;
   fa2::BwdParams p{q, k, v, o, lse, dout, dq, dk, dv,
-                   (float*)ws, (float*)(ws + fa2::bwd_delta_bytes(B, H, N)),
+                   (float*)ws, atomic_dq ? (float*)(ws + fa2::bwd_delta_bytes(B, H, N)) : nullptr,
                    B, H, N, d, causal != 0, scale, (hipStream_t)stream};
-  return fa2::launch_bwd(p) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+  const hipError_t e = atomic_dq ? fa2::launch_bwd_atomic_dq(p) : fa2::launch_bwd(p);
+  return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, void* workspace,
+            size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
+            void* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                    causal, scale, stream, false);
+}
+
+int fa2_bwd_atomic_dq(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                      int causal, float scale, void* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                    causal, scale, stream, true);
 }
 
 }  // extern "C"

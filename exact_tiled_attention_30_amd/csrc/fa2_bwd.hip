@@ -4,8 +4,11 @@
 //   * P is not stored by the forward pass; it is recomputed from the saved
 //     logsumexp L (section 7.1): P = exp(scale * q.k - L).
 //   * The outer loop runs over key/value tiles: the workgroup that holds K_j,
-//     V_j accumulates dK_j and dV_j by itself with no atomics; dQ is summed
-//     across workgroups -- here with fp32 atomics into a workspace (section 7.2).
+//     V_j accumulates dK_j and dV_j by itself with no atomics.  dQ needs a sum
+//     across those workgroups (section 7.2, "atomic add or a two-pass scan");
+//     both are built: a separate Q-outer dQ pass (launch_bwd, the default:
+//     deterministic and faster on MI355X) and fp32 atomics into a workspace
+//     accumulator (launch_bwd_atomic_dq).
 //   * D_i = rowsum(dO_i * O_i) is computed once by a separate pre-processing
 //     kernel (section 7.3) instead of tile by tile inside the main loop.
 // Gradient formulas (lost in the page's extraction; the standard softmax
@@ -21,8 +24,9 @@
 //   * S = K Q^T and dP = V dO^T put the key on the lane, so P and dS feed the
 //     dV += P dO and dK += dS Q products straight from registers (as A
 //     operands), with dO^T and Q^T read transposed from the same row-major
-//     LDS tiles; dS also goes to LDS, from which the workgroup forms its dQ
-//     partial = dS K over its 128 keys and adds it atomically.
+//     LDS tiles; with the atomic dQ strategy, dS also goes to LDS, from which
+//     the workgroup forms its dQ partial = dS K over its 128 keys and adds it
+//     atomically.
 #include <limits.h>
 #include <math.h>
 
@@ -39,7 +43,7 @@ constexpr int kBwdQueries = 64;  // queries per inner step
 // ---------------------------------------------------------------- B0 ----
 // D[b, h, i] = sum_c dO[b, i, h, c] * O[b, i, h, c] (fp32), and zero the dQ
 // accumulator row.  One 16-lane group per (b, i, h) row.
-template <int D>
+template <int D, bool ZERO_DQ>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
     float* __restrict__ delta, float* __restrict__ dq_acc, int H, int N, long long rows) {
@@ -58,8 +62,10 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
         acc += __uint_as_float(a[t] << 16) * __uint_as_float(g[t] << 16);
         acc += __uint_as_float(a[t] & 0xffff0000u) * __uint_as_float(g[t] & 0xffff0000u);
       }
-      *(f32x4*)(dq_acc + base) = f32x4{};
-      *(f32x4*)(dq_acc + base + 4) = f32x4{};
+      if (ZERO_DQ) {
+        *(f32x4*)(dq_acc + base) = f32x4{};
+        *(f32x4*)(dq_acc + base + 4) = f32x4{};
+      }
     } else {
       const u32x2 a = *(const u32x2*)(o + base);
       const u32x2 g = *(const u32x2*)(dout + base);
@@ -68,7 +74,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
         acc += __uint_as_float(a[t] << 16) * __uint_as_float(g[t] << 16);
         acc += __uint_as_float(a[t] & 0xffff0000u) * __uint_as_float(g[t] & 0xffff0000u);
       }
-      *(f32x4*)(dq_acc + base) = f32x4{};
+      if (ZERO_DQ) *(f32x4*)(dq_acc + base) = f32x4{};
     }
   }
   // reduce over the 16 lanes of the row
@@ -156,6 +162,21 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint8_t* tile, const uint32_t (&
   return as_bf16x8(u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
 }
 
+// Scheduling request for an unrolled run of N_MFMA MFMAs, each fed by PER
+// LDS reads: issue the reads AHEAD MFMAs early, then alternate, so the read
+// latency hides behind the matrix pipe (one wave per SIMD here: no other
+// wave covers it).
+template <int N_MFMA, int PER, int AHEAD>
+__device__ __forceinline__ void interleave_lds_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, PER * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N_MFMA - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 // Hides a value from loop-invariant code motion, so addresses derived from
 // it are formed where they are used instead of being hoisted and held live.
 __device__ __forceinline__ uint32_t opaque(uint32_t x) {
@@ -163,7 +184,7 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   return x;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool ATOMIC_DQ>
 __global__ __launch_bounds__(256) void bwd_dl_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
@@ -180,12 +201,12 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(
   constexpr int NKI = KT / 1024 / 4;         // K DMA instructions per wave
   static_assert(NQI >= 1 && NKI >= 1, "tile split");
   using SW = BwdSwz<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t kt_s[KT];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt_s[ATOMIC_DQ ? KT : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t q_s0[QT];
   __shared__ __attribute__((aligned(1024))) uint8_t q_s1[QT];
   __shared__ __attribute__((aligned(1024))) uint8_t do_s0[QT];
   __shared__ __attribute__((aligned(1024))) uint8_t do_s1[QT];
-  __shared__ __attribute__((aligned(1024))) uint8_t ds_s[kBwdKeys * DSB];
+  __shared__ __attribute__((aligned(1024))) uint8_t ds_s[ATOMIC_DQ ? kBwdKeys * DSB : 16];
   __shared__ __attribute__((aligned(256))) float st_s0[2 * kBwdQueries];  // lse | delta
   __shared__ __attribute__((aligned(256))) float st_s1[2 * kBwdQueries];
 
@@ -262,26 +283,58 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(
     }
   };
 
+  // The accumulators start as the result of an MFMA (0 * 0 + 0) rather than
+  // as literal zeros, so the register allocator places them, and keeps them
+  // across the loop, in accumulation registers instead of shuttling them
+  // between register files on every iteration.
   f32x16 dk_acc[D / 32], dv_acc[D / 32];
+  {
+    const bf16x8 z = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    dk_acc[dt] = f32x16{};
-    dv_acc[dt] = f32x16{};
+    for (int dt = 0; dt < D / 32; ++dt) {
+      dk_acc[dt] = mfma32(z, z, f32x16{});
+      dv_acc[dt] = mfma32(z, z, f32x16{});
+    }
   }
 
   const int n_qtiles = (N + kBwdQueries - 1) / kBwdQueries;
   const int it0 = CAUSAL ? j0 / kBwdQueries : 0;
 
 #pragma unroll
-  for (int u = 0; u < NKI; ++u) dma_rows(k, j0, kt_s, wave * NKI + u, lane, [](int r) { return SW::k(r); });
+  for (int u = 0; u < NKI; ++u)
+    if constexpr (ATOMIC_DQ) dma_rows(k, j0, kt_s, wave * NKI + u, lane, [](int r) { return SW::k(r); });
   if (it0 < n_qtiles) issue_step(it0, q_s0, do_s0, st_s0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
+
+  constexpr int kTilesPerWave = D / 64;  // 32x32 dQ tiles per wave per step
+  f32x16 dq_pend[kTilesPerWave];
+  int q0_pend = -1;  // first query of the pending dQ partial (-1: none)
+  auto flush_dq = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kTilesPerWave; ++u) {
+      const int tile = wave * kTilesPerWave + u;
+      const int t = tile % 2, dt = tile / 2;
+      float* dst = dq_acc + head + (size_t)(q0_pend + t * 32) * tok + dt * 32;
+      const int lane_off = 4 * hi * (int)tok + l32;
+      if (q0_pend + kBwdQueries <= N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          atomicAdd(dst + (8 * (r / 4) + r % 4) * tok + lane_off, dq_pend[u][r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (q0_pend + t * 32 + acc_row(r, hi) < N)
+            atomicAdd(dst + (8 * (r / 4) + r % 4) * tok + lane_off, dq_pend[u][r]);
+      }
+    }
+  };
 
   auto step = [&](int it, const uint8_t* qs, const uint8_t* dos, const float* st, uint8_t* qn,
                   uint8_t* don, float* stn) __attribute__((always_inline)) {
     const int q0 = it * kBwdQueries;
     if (it + 1 < n_qtiles) issue_step(it + 1, qn, don, stn);
+    if constexpr (ATOMIC_DQ) if (q0_pend >= 0) flush_dq();
     row_base = opaque(row_base);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -306,6 +359,7 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(
         s[t] = mfma32(*(const bf16x8*)(qs + off), kf[cc], s[t]);
         dp[t] = mfma32(*(const bf16x8*)(dos + off), vf[cc], dp[t]);
       }
+    interleave_lds_mfma<4 * (D / 16), 1, 4>();
 
     // P = exp2(S*c - L*log2e), dS = P * (dP - D); masked entries are 0.
     // Entry (t, g, e) is query q0 + 4*hi + C with C = t*32 + 8*g + e, visible
@@ -348,7 +402,9 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(
         dk_acc[dt] = mfma32(dsf, tr_frag<RB>(qs, trq, dt, cc), dk_acc[dt]);
       }
     }
+    interleave_lds_mfma<2 * (kBwdQueries / 16) * (D / 32), 2, 3>();
 
+    if constexpr (ATOMIC_DQ) {
     // dS (bf16) -> LDS [key][query], 4 consecutive queries per 8-byte store
     {
 #pragma unroll
@@ -362,8 +418,9 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(
     }
     __syncthreads();
 
-    // dQ partial = scale * dS K over this workgroup's 128 keys, added atomically
-    constexpr int kTilesPerWave = D / 64;
+    // dQ partial = scale * dS K over this workgroup's 128 keys.  Its atomic
+    // adds are issued at the start of the next step (flush_dq), so their
+    // round trips overlap that step's work instead of the wait below.
 #pragma unroll
     for (int u = 0; u < kTilesPerWave; ++u) {
       const int tile = wave * kTilesPerWave + u;
@@ -375,18 +432,10 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(
         const bf16x8 bk = tr_frag<RB>(kt_s, trk, dt, cc);
         acc = mfma32(a, bk, acc);
       }
-      float* dst = dq_acc + head + (size_t)(q0 + t * 32) * tok + dt * 32;
-      const int lane_off = 4 * hi * (int)tok + l32;
-      if (q0 + kBwdQueries <= N) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          atomicAdd(dst + (8 * (r / 4) + r % 4) * tok + lane_off, scale * acc[r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (q0 + t * 32 + acc_row(r, hi) < N)
-            atomicAdd(dst + (8 * (r / 4) + r % 4) * tok + lane_off, scale * acc[r]);
-      }
+      interleave_lds_mfma<kBwdKeys / 16, 4, 2>();
+      dq_pend[u] = acc * scale;
+    }
+    q0_pend = q0;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // next step's tiles have landed
     __syncthreads();
@@ -395,6 +444,7 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(
     step(it, q_s0, do_s0, st_s0, q_s1, do_s1, st_s1);
     if (it + 1 < n_qtiles) step(it + 1, q_s1, do_s1, st_s1, q_s0, do_s0, st_s0);
   }
+  if constexpr (ATOMIC_DQ) if (q0_pend >= 0) flush_dq();
 
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -409,42 +459,283 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(
     }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_bwd_t(const BwdParams& p) {
+// ----------------------------------------------------------- B2 (dQ) ----
+// Q-outer dQ pass, the two-pass alternative to the atomic dQ sum (infra-guide
+// page "6.2 FlashAttention V2 in depth", section 7.2, "a two-pass scan", read
+// as a separate pass over Q tiles).  Shaped like the forward pass: a wave
+// owns 32 query rows (Q and dO rows held in VGPRs as MFMA B operands, L and D
+// as per-lane scalars) and walks the visible K/V tiles, double-buffered in
+// LDS by DMA.  Per tile it recomputes S^T = K Q^T and dP^T = V dO^T, forms
+// P^T = exp2(S^T c - L log2 e) and dS^T = P^T (dP^T - D) with the query on
+// the lane, and accumulates dQ^T += K^T dS^T, reading K^T transposed from the
+// same row-major K tile.  No atomics and no fp32 workspace: each dQ row is
+// written once, in bf16, so the result is deterministic.
+template <int D>
+struct DqSwz {
+  // K tile: row reads (A of S^T) and transposed reads (A of dQ^T)
+  __device__ static constexpr int k(int r) { return BwdSwz<D>::qd(r); }
+  // V tile: row reads only
+  __device__ static constexpr int v(int r) { return D == 128 ? (r % 16) : ((r / 2) % 8); }
+};
+
+template <int D, int W, bool CAUSAL>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W))) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dq,
+    int H, int N, int n_qtiles, int grid, float c, float scale) {
+  constexpr int BC = 64;                    // keys per K/V tile
+  constexpr int BR = W * 32;                // query rows per Q tile
+  constexpr int RB = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 1024 / RB;
+  constexpr int TILE = BC * RB;
+  constexpr int NI = TILE / 1024;
+  constexpr int NIW = NI / W;
+  static_assert(NI % W == 0 && NIW >= 1, "tile split");
+  using SW = DqSwz<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1[TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int l32 = lane % 32, hi = lane / 32;
+
+  // causal work items pair a heavy and a light Q tile, as in the forward pass
+  const int logical = xcd_contiguous_id(blockIdx.x, grid);
+  const int per_head = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+  const int bh = logical / per_head;
+  const int item = logical % per_head;
+  const int n_pass = (CAUSAL && item != n_qtiles - 1 - item) ? 2 : 1;
+  const int b = bh / H, hh = bh % H;
+  const size_t tok = (size_t)H * D;
+  const size_t head = (size_t)b * N * tok + (size_t)hh * D;
+  const size_t rowstat = ((size_t)b * H + hh) * N;
+
+  uint32_t koff[NIW], voff[NIW];
+  int lrow[NIW];
+#pragma unroll
+  for (int u = 0; u < NIW; ++u) {
+    const int m = wave * NIW + u;
+    const int r = m * RPI + lane / CPR, slot = lane % CPR;
+    lrow[u] = r;
+    koff[u] = (uint32_t)(r * tok * 2) + (uint32_t)((slot ^ SW::k(r)) * 16);
+    voff[u] = (uint32_t)(r * tok * 2) + (uint32_t)((slot ^ SW::v(r)) * 16);
+  }
+  auto issue = [&](int jt, uint8_t* kd, uint8_t* vd) __attribute__((always_inline)) {
+    const int kv0 = jt * BC;
+    const uint8_t* kbase = (const uint8_t*)(k + head + (size_t)kv0 * tok);
+    const uint8_t* vbase = (const uint8_t*)(v + head + (size_t)kv0 * tok);
+    const bool whole = kv0 + BC <= N;
+#pragma unroll
+    for (int u = 0; u < NIW; ++u) {
+      const int m = wave * NIW + u;
+      uint32_t ko = koff[u], vo = voff[u];
+      if (!whole) {
+        const uint32_t back = (uint32_t)(max(kv0 + lrow[u] - (N - 1), 0) * tok * 2);
+        ko -= back;
+        vo -= back;
+      }
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kbase + ko),
+                                       (void __attribute__((address_space(3)))*)(kd + m * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vbase + vo),
+                                       (void __attribute__((address_space(3)))*)(vd + m * 1024), 16, 0, 0);
+    }
+  };
+
+  // LDS read offsets: K / V row kt*32 + l%32, chunk 2*cc + hi at
+  // (base ^ (cc << 5)) + kt*32*RB; K^T fragment (cc, dt), half u at
+  // (ktr[u] ^ (dt << 6)) + cc*16*RB.
+  uint32_t k_row = (uint32_t)(l32 * RB + ((hi ^ SW::k(l32)) * 16));
+  uint32_t v_row = (uint32_t)(l32 * RB + ((hi ^ SW::v(l32)) * 16));
+  uint32_t ktr[2];
+  tr_offsets<RB>(lane, [](int r) { return SW::k(r); }, ktr);
+
+  for (int pass = 0; pass < n_pass; ++pass) {
+    const int qt = CAUSAL ? (pass == 0 ? n_qtiles - 1 - item : item) : item;
+    const int q0 = qt * BR;
+    const int qw0 = q0 + wave * 32;
+    const int my_q = qw0 + l32;
+    const int qc = min(my_q, N - 1);
+
+    bf16x8 qf[D / 16], dof[D / 16];
+    {
+      const uint16_t* qp = q + head + (size_t)qc * tok + 8 * hi;
+      const uint16_t* dp_ = dout + head + (size_t)qc * tok + 8 * hi;
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) {
+        u32x4 x = *(const u32x4*)(qp + 16 * cc);
+        u32x4 y = *(const u32x4*)(dp_ + 16 * cc);
+        if (my_q >= N) x = y = u32x4{0u, 0u, 0u, 0u};
+        qf[cc] = as_bf16x8(x);
+        dof[cc] = as_bf16x8(y);
+      }
+    }
+    const float l2 = lse[rowstat + qc] * kLog2e;
+    const float dd = delta[rowstat + qc];
+
+    const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+    const int n_kv = (kv_len + BC - 1) / BC;
+
+    f32x16 dqa[D / 32];
+    {
+      const bf16x8 z = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = mfma32(z, z, f32x16{});
+    }
+
+    auto tile = [&](int jt, const uint8_t* kb, const uint8_t* vb) __attribute__((always_inline)) {
+      const int kv0 = jt * BC;
+      k_row = opaque(k_row);
+      v_row = opaque(v_row);
+      ktr[0] = opaque(ktr[0]);
+      ktr[1] = opaque(ktr[1]);
+      f32x16 s[BC / 32], dp[BC / 32];
+#pragma unroll
+      for (int kt = 0; kt < BC / 32; ++kt) {
+        s[kt] = f32x16{};
+        dp[kt] = f32x16{};
+      }
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc)
+#pragma unroll
+        for (int kt = 0; kt < BC / 32; ++kt) {
+          const uint32_t ko = (k_row ^ (uint32_t)(cc << 5)) + kt * 32 * RB;
+          const uint32_t vo = (v_row ^ (uint32_t)(cc << 5)) + kt * 32 * RB;
+          s[kt] = mfma32(*(const bf16x8*)(kb + ko), qf[cc], s[kt]);
+          dp[kt] = mfma32(*(const bf16x8*)(vb + vo), dof[cc], dp[kt]);
+        }
+      interleave_lds_mfma<2 * (D / 16) * (BC / 32), 1, 4>();
+
+      // P^T, dS^T (query on the lane); keys past the diagonal or N give 0
+      const bool need_mask = (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N);
+#pragma unroll
+      for (int kt = 0; kt < BC / 32; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = fast_exp2(fmaf(s[kt][r], c, -l2));
+          if (need_mask) {
+            const int key = kv0 + kt * 32 + acc_row(r, hi);
+            if (!(key < N && (!CAUSAL || key <= my_q))) pr = 0.f;
+          }
+          dp[kt][r] = pr * (dp[kt][r] - dd);
+        }
+
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int cc = 0; cc < BC / 16; ++cc) {
+        const f32x16& sv = dp[cc / 2];
+        const int r0 = 8 * (cc % 2);
+        const bf16x8 dsf = to_bf16x8(f32x8{sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
+                                           sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]});
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = mfma32(tr_frag<RB>(kb, ktr, dt, cc), dsf, dqa[dt]);
+      }
+      interleave_lds_mfma<(BC / 16) * (D / 32), 2, 3>();
+    };
+
+    if (n_kv > 0) issue(0, kb0, vb0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 has landed
+    __syncthreads();
+    auto step = [&](int jt, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn)
+        __attribute__((always_inline)) {
+      issue(min(jt + 1, n_kv - 1), kn, vn);
+      if (!CAUSAL || jt * BC <= qw0 + 31) tile(jt, kc, vc);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile jt+1 has landed
+      __syncthreads();
+    };
+    for (int jt = 0; jt < n_kv; jt += 2) {
+      step(jt, kb0, vb0, kb1, vb1);
+      if (jt + 1 < n_kv) step(jt + 1, kb1, vb1, kb0, vb0);
+    }
+
+    if (my_q < N) {
+      uint16_t* op = dq + head + (size_t)my_q * tok;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = f32x4{dqa[dt][4 * g + 0], dqa[dt][4 * g + 1], dqa[dt][4 * g + 2],
+                                dqa[dt][4 * g + 3]} * scale;
+          *(u32x2*)(op + dt * 32 + 8 * g + 4 * hi) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+        }
+    }
+  }
+}
+
+// B0 launch: D (and, for the atomic dQ sum, the zeroed accumulator)
+template <int D, bool ZERO_DQ>
+void launch_preprocess(const BwdParams& p) {
   const long long rows = (long long)p.B * p.N * p.H;
+  const long long blocks = (rows + 15) / 16;
+  hipLaunchKernelGGL((bwd_preprocess_kernel<D, ZERO_DQ>), dim3((unsigned)blocks), dim3(256), 0,
+                     p.stream, (const uint16_t*)p.o, (const uint16_t*)p.dout, p.delta, p.dq_acc,
+                     p.H, p.N, rows);
+}
+
+template <int D, bool CAUSAL, bool ATOMIC_DQ>
+void launch_kv_outer(const BwdParams& p) {
+  const int n_ktiles = (p.N + kBwdKeys - 1) / kBwdKeys;
+  const long long grid = (long long)p.B * p.H * n_ktiles;
+  const float c = (float)((double)p.scale * 1.4426950408889634);
+  hipLaunchKernelGGL((bwd_dl_kernel<D, CAUSAL, ATOMIC_DQ>), dim3((unsigned)grid), dim3(kBwdThreads),
+                     0, p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
+                     (const uint16_t*)p.dout, p.lse, p.delta, p.dq_acc, (uint16_t*)p.dk,
+                     (uint16_t*)p.dv, p.H, p.N, n_ktiles, (int)grid, c, p.scale);
+}
+
+template <int D, int W, bool CAUSAL>
+void launch_dq_pass(const BwdParams& p) {
+  constexpr int BR = W * 32;
+  const int n_qtiles = (p.N + BR - 1) / BR;
+  const long long grid = (long long)p.B * p.H * (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
+  const float c = (float)((double)p.scale * 1.4426950408889634);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, W, CAUSAL>), dim3((unsigned)grid), dim3(W * 64), 0, p.stream,
+                     (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
+                     (const uint16_t*)p.dout, p.lse, p.delta, (uint16_t*)p.dq, p.H, p.N, n_qtiles,
+                     (int)grid, c, p.scale);
+}
+
+// dQ summed with fp32 atomics across the KV-outer workgroups, then converted
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_atomic(const BwdParams& p) {
   (void)hipGetLastError();
-  // B0: D vector and dQ accumulator reset
-  {
-    const long long blocks = (rows + 15) / 16;
-    hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)blocks), dim3(256), 0,
-                       p.stream, (const uint16_t*)p.o, (const uint16_t*)p.dout, p.delta,
-                       p.dq_acc, p.H, p.N, rows);
-  }
-  // B1: main KV-outer kernel
-  {
-    const int n_ktiles = (p.N + kBwdKeys - 1) / kBwdKeys;
-    const long long grid = (long long)p.B * p.H * n_ktiles;
-    const float c = (float)((double)p.scale * 1.4426950408889634);
-    hipLaunchKernelGGL((bwd_dl_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kBwdThreads), 0,
-                       p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
-                       (const uint16_t*)p.v, (const uint16_t*)p.dout, p.lse, p.delta,
-                       p.dq_acc, (uint16_t*)p.dk, (uint16_t*)p.dv, p.H, p.N, n_ktiles,
-                       (int)grid, c, p.scale);
-  }
-  // B2: dQ to bf16
-  {
-    const long long n8 = rows * D / 8;
-    hipLaunchKernelGGL(bwd_convert_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
-                       p.stream, p.dq_acc, (uint16_t*)p.dq, n8);
-  }
+  launch_preprocess<D, true>(p);
+  launch_kv_outer<D, CAUSAL, true>(p);
+  const long long n8 = (long long)p.B * p.N * p.H * D / 8;
+  hipLaunchKernelGGL(bwd_convert_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                     p.stream, p.dq_acc, (uint16_t*)p.dq, n8);
+  return hipGetLastError();
+}
+
+// dQ from its own Q-outer pass (no atomics, no fp32 accumulator)
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_two_pass(const BwdParams& p) {
+  (void)hipGetLastError();
+  launch_preprocess<D, false>(p);
+  launch_kv_outer<D, CAUSAL, false>(p);
+  constexpr int kCus = 256;
+  const long long items8 =
+      (long long)p.B * p.H * (CAUSAL ? ((p.N + 255) / 256 + 1) / 2 : (p.N + 255) / 256);
+  if (items8 < 2 * kCus) launch_dq_pass<D, 4, CAUSAL>(p);
+  else launch_dq_pass<D, 8, CAUSAL>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdParams& p) {
-  if (p.d == 64) return p.causal ? launch_bwd_t<64, true>(p) : launch_bwd_t<64, false>(p);
-  return p.causal ? launch_bwd_t<128, true>(p) : launch_bwd_t<128, false>(p);
+  if (p.d == 64)
+    return p.causal ? launch_bwd_two_pass<64, true>(p) : launch_bwd_two_pass<64, false>(p);
+  return p.causal ? launch_bwd_two_pass<128, true>(p) : launch_bwd_two_pass<128, false>(p);
+}
+
+hipError_t launch_bwd_atomic_dq(const BwdParams& p) {
+  if (p.d == 64)
+    return p.causal ? launch_bwd_atomic<64, true>(p) : launch_bwd_atomic<64, false>(p);
+  return p.causal ? launch_bwd_atomic<128, true>(p) : launch_bwd_atomic<128, false>(p);
 }
 
 }  // namespace fa2

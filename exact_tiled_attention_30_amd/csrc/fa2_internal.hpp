@@ -30,7 +30,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;   // D vector, fp32 [B, H, N] (workspace)
-  float* dq_acc;  // fp32 [B, N, H, d] (workspace)
+  float* dq_acc;  // fp32 [B, N, H, d] (workspace; atomic dQ strategy only)
   int B, H, N, d;
   bool causal;
   float scale;
@@ -42,6 +42,7 @@ size_t bwd_delta_bytes(int B, int H, int N);
 size_t bwd_dq_acc_bytes(int B, int H, int N, int d);
 
 hipError_t launch_fwd(const FwdParams& p);
-hipError_t launch_bwd(const BwdParams& p);
+hipError_t launch_bwd(const BwdParams& p);             // dQ from a Q-outer pass
+hipError_t launch_bwd_atomic_dq(const BwdParams& p);   // dQ summed with fp32 atomics
 
 }  // namespace fa2

@@ -72,16 +72,18 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace fa2_bwd needs for these sizes (0 if the problem
- * is empty or the arguments are invalid).  Holds the D vector (fp32 [B,H,N])
- * and an fp32 dQ accumulator ([B, N, H, d]).
+ * is empty or the arguments are invalid): the D vector, fp32 [B, H, N].
  */
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d, int causal);
 
 /*
  * Backward pass ("6.2 FlashAttention V2 in depth", section 7: P is recovered
  * from the saved logsumexp, dK and dV are owned by the block that holds a
- * key/value tile, dQ is summed across blocks, and D_i = rowsum(dO_i * O_i) is
- * computed once by a separate pre-processing kernel).
+ * key/value tile, and D_i = rowsum(dO_i * O_i) is computed once by a separate
+ * pre-processing kernel).  dQ, which section 7.2 says must be summed across
+ * the blocks of different key/value tiles, comes from a second pass over Q
+ * tiles (the page's "two-pass" option): no atomics, and the result is
+ * bitwise reproducible run to run.
  *   q, k, v : forward inputs, bf16 [B, N, H, d]
  *   o, lse  : forward outputs of fa2_fwd for the same q, k, v, causal, scale
  *   dout    : gradient of the loss w.r.t. o, bf16 [B, N, H, d]
@@ -96,6 +98,27 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o,
             const float* lse, const void* dout, void* dq, void* dk, void* dv,
             void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
             int causal, float scale, void* stream);
+
+/*
+ * Bytes of device workspace fa2_bwd_atomic_dq needs (0 if the problem is
+ * empty or the arguments are invalid): the D vector (fp32 [B, H, N]) and an
+ * fp32 dQ accumulator ([B, N, H, d]), each 256-byte aligned.
+ */
+size_t fa2_bwd_atomic_dq_workspace_bytes(int B, int H, int N, int d, int causal);
+
+/*
+ * The same backward pass with section 7.2's other option for dQ: every
+ * key/value block adds its dQ partial into the fp32 accumulator in the
+ * workspace with atomic adds, and a final kernel rounds it to bf16.  dK and
+ * dV are bitwise reproducible; dQ may differ in the last bits between runs
+ * (the order of the fp32 additions varies).  Arguments, layouts, ownership
+ * and errors as for fa2_bwd, except that the workspace must hold at least
+ * fa2_bwd_atomic_dq_workspace_bytes() bytes.
+ */
+int fa2_bwd_atomic_dq(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                      int causal, float scale, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa2_status_string(int status);

@@ -36,8 +36,9 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_fwd",
-                                    "fa2_status_string"]
+    assert declared_functions() == ["fa2_bwd", "fa2_bwd_atomic_dq",
+                                    "fa2_bwd_atomic_dq_workspace_bytes",
+                                    "fa2_bwd_workspace_bytes", "fa2_fwd", "fa2_status_string"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -95,34 +96,45 @@ def test_bwd_workspace_size(L):
     for (B, H, N, d) in ((1, 1, 1, 64), (4, 16, 4096, 128), (2, 3, 257, 64)):
         want_d = (B * H * N * 4 + 255) // 256 * 256
         want_q = (B * H * N * d * 4 + 255) // 256 * 256
-        assert binding.fa2_bwd_workspace_bytes(B, H, N, d, True) == want_d + want_q
-    assert binding.fa2_bwd_workspace_bytes(0, 1, 1, 64, False) == 0
-    assert binding.fa2_bwd_workspace_bytes(1, 1, 1, 80, False) == 0
-    assert binding.fa2_bwd_workspace_bytes(-1, 1, 1, 64, False) == 0
+        assert binding.fa2_bwd_workspace_bytes(B, H, N, d, True) == want_d
+        assert binding.fa2_bwd_atomic_dq_workspace_bytes(B, H, N, d, True) == want_d + want_q
+    for f in (binding.fa2_bwd_workspace_bytes, binding.fa2_bwd_atomic_dq_workspace_bytes):
+        assert f(0, 1, 1, 64, False) == 0
+        assert f(1, 1, 1, 80, False) == 0
+        assert f(-1, 1, 1, 64, False) == 0
 
 
-def bwd(L, B=2, H=3, N=100, d=64, causal=1, scale=0.125, ws_bytes=None, **ptrs):
+def bwd(L, B=2, H=3, N=100, d=64, causal=1, scale=0.125, ws_bytes=None, atomic=False, **ptrs):
     p = dict(q=Q, k=K, v=V, o=O, lse=LSE, dout=DO, dq=DQ, dk=DK, dv=DV, ws=WS)
     p.update(ptrs)
+    sizer = L.fa2_bwd_atomic_dq_workspace_bytes if atomic else L.fa2_bwd_workspace_bytes
     if ws_bytes is None:
-        ws_bytes = L.fa2_bwd_workspace_bytes(B, H, N, d, causal)
-    return L.fa2_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"], p["dk"],
-                     p["dv"], p["ws"], ws_bytes, B, H, N, d, causal, ctypes.c_float(scale),
-                     None)
+        ws_bytes = sizer(B, H, N, d, causal)
+    fn = L.fa2_bwd_atomic_dq if atomic else L.fa2_bwd
+    return fn(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"], p["dk"], p["dv"],
+              p["ws"], ws_bytes, B, H, N, d, causal, ctypes.c_float(scale), None)
 
 
-def test_bwd_argument_errors(L):
-    assert bwd(L, N=-1) == SHAPE
-    assert bwd(L, d=32) == HEADDIM
-    assert bwd(L, scale=-math.inf) == SCALE
+@pytest.mark.parametrize("atomic", [False, True], ids=["two_pass", "atomic_dq"])
+def test_bwd_argument_errors(L, atomic):
+    assert bwd(L, N=-1, atomic=atomic) == SHAPE
+    assert bwd(L, d=32, atomic=atomic) == HEADDIM
+    assert bwd(L, scale=-math.inf, atomic=atomic) == SCALE
     for name in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv"):
-        assert bwd(L, **{name: None}) == NULLPTR, name
-    assert bwd(L, ws=None) == WORKSPACE
+        assert bwd(L, atomic=atomic, **{name: None}) == NULLPTR, name
+    assert bwd(L, ws=None, atomic=atomic) == WORKSPACE
+    sizer = L.fa2_bwd_atomic_dq_workspace_bytes if atomic else L.fa2_bwd_workspace_bytes
+    need = sizer(2, 3, 100, 64, 1)
+    assert bwd(L, ws_bytes=need - 1, atomic=atomic) == WORKSPACE
+    assert bwd(L, dq=DQ + 4, atomic=atomic) == ALIGN
+    assert bwd(L, ws=WS + 8, atomic=atomic) == ALIGN
+    assert bwd(L, dk=K, atomic=atomic) == ALIAS
+    assert bwd(L, dv=DQ + 64, atomic=atomic) == ALIAS
+    assert bwd(L, ws=DO, atomic=atomic) == ALIAS
+    assert bwd(L, N=0, q=None, ws=None, atomic=atomic) == OK
+
+
+def test_atomic_workspace_is_larger(L):
+    # the two-pass backward's workspace is too small for the atomic one
     need = L.fa2_bwd_workspace_bytes(2, 3, 100, 64, 1)
-    assert bwd(L, ws_bytes=need - 1) == WORKSPACE
-    assert bwd(L, dq=DQ + 4) == ALIGN
-    assert bwd(L, ws=WS + 8) == ALIGN
-    assert bwd(L, dk=K) == ALIAS
-    assert bwd(L, dv=DQ + 64) == ALIAS
-    assert bwd(L, ws=DO) == ALIAS
-    assert bwd(L, N=0, q=None, ws=None) == OK
+    assert bwd(L, ws_bytes=need, atomic=True) == WORKSPACE

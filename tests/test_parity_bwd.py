@@ -1,7 +1,8 @@
 """GPU parity of the backward pass against the fp64 oracle.
 
-O and L come from this library's forward pass (fa2_fwd), as the backward
-would be used.  Small shapes are compared in full; the full-size backward
+Both dQ strategies are covered: fa2_bwd (dQ from a Q-outer pass) and
+fa2_bwd_atomic_dq (dQ summed with fp32 atomics).  O and L come from this
+library's forward pass (fa2_fwd), as the backward would be used.  Small shapes are compared in full; the full-size backward
 workload (B=4, H=16, N=4096, d=128, causal) is compared on whole heads -- the
 oracle's backward of a head is independent of the others.  Tolerances
 (oracle/compare.py): per gradient, max |dG| <= 5e-2 max |G_ref| and
@@ -20,11 +21,15 @@ from oracle.compare import gradient_report
 pytestmark = pytest.mark.gpu
 
 
-def run_bwd(x, causal, scale):
+STRATEGIES = [False, True]
+STRATEGY_IDS = ["two_pass", "atomic_dq"]
+
+
+def run_bwd(x, causal, scale, atomic_dq=False):
     d = {n: t.cuda() for n, t in x.items()}
     o, lse = binding.attention_forward(d["q"], d["k"], d["v"], causal, scale)
     dq, dk, dv = binding.attention_backward(d["q"], d["k"], d["v"], o, lse, d["dout"], causal,
-                                            scale)
+                                            scale, atomic_dq=atomic_dq)
     torch.cuda.synchronize()
     return dq.cpu(), dk.cpu(), dv.cpu()
 
@@ -57,14 +62,15 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("atomic_dq", STRATEGIES, ids=STRATEGY_IDS)
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "b{}h{}n{}d{}".format(*s))
-def test_small_shapes_every_element(shape, causal):
+def test_small_shapes_every_element(shape, causal, atomic_dq):
     B, H, N, d = shape
     scale = d ** -0.5
-    print(f"[bwd small] shape={shape} causal={causal}", flush=True)
+    print(f"[bwd small] shape={shape} causal={causal} atomic_dq={atomic_dq}", flush=True)
     x = make_inputs(B, H, N, d, seed=21, with_dout=True)
-    grads = run_bwd(x, causal, scale)
+    grads = run_bwd(x, causal, scale, atomic_dq)
     heads = [(b, h) for b in range(B) for h in range(H)]
     ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["dout"], causal, scale, heads)
     check(grads, ref, heads, f"{shape} causal={causal}")
@@ -93,26 +99,52 @@ def test_gradient_sums_on_gpu():
     assert (((dv.sum(dim=1) - do.sum(dim=1)).abs()) <= 1e-2 * do.abs().sum(dim=1)).all()
 
 
-def test_full_size_backward_workload_heads():
+@pytest.mark.parametrize("atomic_dq", STRATEGIES, ids=STRATEGY_IDS)
+def test_full_size_backward_workload_heads(atomic_dq):
     w = WORKLOADS["bwd_b4_h16_n4096_d128_causal"]
-    print(f"[bwd full-size] {w.name}", flush=True)
+    print(f"[bwd full-size] {w.name} atomic_dq={atomic_dq}", flush=True)
     x = make_inputs(w.B, w.H, w.N, w.d, seed=w.seed, with_dout=True)
-    grads = run_bwd(x, w.causal, w.scale)
+    grads = run_bwd(x, w.causal, w.scale, atomic_dq)
     heads = [(0, 0), (3, 15), (1, 7), (2, 3)]
     ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["dout"], w.causal, w.scale, heads)
     check(grads, ref, heads, w.name)
 
 
-def test_backward_is_deterministic_in_dk_dv():
-    # dK and dV are owned by one workgroup each (no atomics): bitwise stable.
+def test_two_pass_backward_is_bitwise_deterministic():
+    # no atomics anywhere: every output is written once, in a fixed order
     B, H, N, d = 2, 2, 300, 64
     x = {n: t.cuda() for n, t in make_inputs(B, H, N, d, seed=2, with_dout=True).items()}
     o, lse = binding.attention_forward(x["q"], x["k"], x["v"], True, 0.125)
     r1 = binding.attention_backward(x["q"], x["k"], x["v"], o, lse, x["dout"], True, 0.125)
     r2 = binding.attention_backward(x["q"], x["k"], x["v"], o, lse, x["dout"], True, 0.125)
     torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_atomic_dq_backward_is_deterministic_in_dk_dv():
+    # dK and dV are owned by one workgroup each (no atomics): bitwise stable.
+    B, H, N, d = 2, 2, 300, 64
+    x = {n: t.cuda() for n, t in make_inputs(B, H, N, d, seed=2, with_dout=True).items()}
+    o, lse = binding.attention_forward(x["q"], x["k"], x["v"], True, 0.125)
+    r1 = binding.attention_backward(x["q"], x["k"], x["v"], o, lse, x["dout"], True, 0.125,
+                                    atomic_dq=True)
+    r2 = binding.attention_backward(x["q"], x["k"], x["v"], o, lse, x["dout"], True, 0.125,
+                                    atomic_dq=True)
+    torch.cuda.synchronize()
     assert torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
     # dQ is summed with atomics: equal up to fp32 reassociation before rounding
     diff = (r1[0].float() - r2[0].float()).abs().max().item()
     assert diff <= 1e-2 * r1[0].float().abs().max().item()
     assert np.isfinite(r1[0].float().cpu().numpy()).all()
+
+
+def test_strategies_agree():
+    # the two dQ strategies sum the same products in different orders
+    B, H, N, d = 1, 4, 520, 128
+    x = make_inputs(B, H, N, d, seed=9, with_dout=True)
+    a = run_bwd(x, True, d ** -0.5, False)
+    b = run_bwd(x, True, d ** -0.5, True)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    rel = (a[0].float() - b[0].float()).abs().max() / a[0].float().abs().max()
+    assert rel.item() <= 1e-2
