@@ -185,7 +185,7 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
 }
 
 template <int D, bool CAUSAL, bool ATOMIC_DQ>
-__global__ __launch_bounds__(256) void bwd_dl_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dl_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dq_acc,
@@ -344,32 +344,27 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(
     }
     dsw_base = opaque(dsw_base);
 
-    // S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = f32x16{};
-      dp[t] = f32x16{};
-    }
-#pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint32_t off = (row_base ^ (uint32_t)(cc << 5)) + t * 32 * RB;
-        s[t] = mfma32(*(const bf16x8*)(qs + off), kf[cc], s[t]);
-        dp[t] = mfma32(*(const bf16x8*)(dos + off), vf[cc], dp[t]);
-      }
-    interleave_lds_mfma<4 * (D / 16), 1, 4>();
-
-    // P = exp2(S*c - L*log2e), dS = P * (dP - D); masked entries are 0.
-    // Entry (t, g, e) is query q0 + 4*hi + C with C = t*32 + 8*g + e, visible
-    // iff lo <= C < hi_lim: two compares against per-lane bounds.
+    // The 64 queries of the step go in two halves of 32, so only one half's
+    // S and dP accumulators are live at a time.
     const bool need_mask =
         (CAUSAL && kw0 + 31 > q0) || (q0 + kBwdQueries > N) || (kw0 + 32 > N);
     const int lo = CAUSAL ? my_key - q0 - 4 * hi : INT_MIN;
     const int hi_lim = my_key < N ? N - q0 - 4 * hi : INT_MIN;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      // S = Q K^T and dP = dO V^T for queries t*32 .. t*32+31 x this wave's 32 keys
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) {
+        const uint32_t off = (row_base ^ (uint32_t)(cc << 5)) + t * 32 * RB;
+        s = mfma32(*(const bf16x8*)(qs + off), kf[cc], s);
+        dp = mfma32(*(const bf16x8*)(dos + off), vf[cc], dp);
+      }
+      interleave_lds_mfma<2 * (D / 16), 1, 4>();
+
+      // P = exp2(S*c - L*log2e), dS = P * (dP - D); masked entries are 0.
+      // Entry (g, e) is query q0 + 4*hi + C with C = t*32 + 8*g + e, visible
+      // iff lo <= C < hi_lim: two compares against per-lane bounds.
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qr = t * 32 + 8 * g + 4 * hi;
@@ -379,43 +374,40 @@ __global__ __launch_bounds__(256) void bwd_dl_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           const int C = t * 32 + 8 * g + e;
-          float pr = fast_exp2(fmaf(s[t][r], c, -l4[e] * kLog2e));
+          float pr = fast_exp2(fmaf(s[r], c, -l4[e] * kLog2e));
           if (need_mask && !(lo <= C && C < hi_lim)) pr = 0.f;
-          s[t][r] = pr;
-          dp[t][r] = pr * (dp[t][r] - d4[e]);
+          s[r] = pr;
+          dp[r] = pr * (dp[r] - d4[e]);
         }
       }
 
-    // dV += P^T dO and dK += dS^T Q: B operands dO^T and Q^T read transposed
+      // dV += P^T dO and dK += dS^T Q: B operands dO^T and Q^T read transposed
 #pragma unroll
-    for (int cc = 0; cc < kBwdQueries / 16; ++cc) {
-      const int r0 = 8 * (cc % 2);
-      const f32x16& sv = s[cc / 2];
-      const f32x16& dsv = dp[cc / 2];
-      const bf16x8 pf = to_bf16x8(f32x8{sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
-                                        sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]});
-      const bf16x8 dsf = to_bf16x8(f32x8{dsv[r0], dsv[r0 + 1], dsv[r0 + 2], dsv[r0 + 3],
-                                         dsv[r0 + 4], dsv[r0 + 5], dsv[r0 + 6], dsv[r0 + 7]});
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int r0 = 8 * c2;
+        const bf16x8 pf = to_bf16x8(f32x8{s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4],
+                                          s[r0 + 5], s[r0 + 6], s[r0 + 7]});
+        const bf16x8 dsf = to_bf16x8(f32x8{dp[r0], dp[r0 + 1], dp[r0 + 2], dp[r0 + 3],
+                                           dp[r0 + 4], dp[r0 + 5], dp[r0 + 6], dp[r0 + 7]});
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dv_acc[dt] = mfma32(pf, tr_frag<RB>(dos, trq, dt, cc), dv_acc[dt]);
-        dk_acc[dt] = mfma32(dsf, tr_frag<RB>(qs, trq, dt, cc), dk_acc[dt]);
+        for (int dt = 0; dt < D / 32; ++dt) {
+          dv_acc[dt] = mfma32(pf, tr_frag<RB>(dos, trq, dt, 2 * t + c2), dv_acc[dt]);
+          dk_acc[dt] = mfma32(dsf, tr_frag<RB>(qs, trq, dt, 2 * t + c2), dk_acc[dt]);
+        }
       }
-    }
-    interleave_lds_mfma<2 * (kBwdQueries / 16) * (D / 32), 2, 3>();
+      interleave_lds_mfma<2 * 2 * (D / 32), 2, 3>();
 
-    if constexpr (ATOMIC_DQ) {
-    // dS (bf16) -> LDS [key][query], 4 consecutive queries per 8-byte store
-    {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
+      if constexpr (ATOMIC_DQ) {
+        // dS (bf16) -> LDS [key][query], 4 consecutive queries per 8-byte store
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const bf16x4 x = to_bf16x4(f32x4{dp[t][4 * g], dp[t][4 * g + 1], dp[t][4 * g + 2],
-                                           dp[t][4 * g + 3]});
+          const bf16x4 x = to_bf16x4(f32x4{dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3]});
           *(u32x2*)(ds_s + (dsw_base ^ (uint32_t)((4 * t + g) << 4))) = __builtin_bit_cast(u32x2, x);
         }
+      }
     }
+
+    if constexpr (ATOMIC_DQ) {
     __syncthreads();
 
     // dQ partial = scale * dS K over this workgroup's 128 keys.  Its atomic
