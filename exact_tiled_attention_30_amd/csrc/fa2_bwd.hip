@@ -214,10 +214,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int l32 = lane % 32, hi = lane / 32;
 
+  // Work item: non-causal, one key tile; causal, the pair (p, n_ktiles-1-p)
+  // of a heavy and a light key tile, so every workgroup walks about the same
+  // number of query steps.
   const int logical = xcd_contiguous_id(blockIdx.x, grid);
-  const int bh = logical / n_ktiles;
-  const int kt_idx = logical % n_ktiles;  // heaviest (first) key tiles first under causal
+  const int per_head = CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles;
+  const int bh = logical / per_head;
+  const int item = logical % per_head;
+  const int n_pass = (CAUSAL && item != n_ktiles - 1 - item) ? 2 : 1;
   const int b = bh / H, hh = bh % H;
+  for (int pass = 0; pass < n_pass; ++pass) {
+  const int kt_idx = pass == 0 ? item : n_ktiles - 1 - item;
   const int j0 = kt_idx * kBwdKeys;
   const int kw0 = j0 + wave * 32;
   const int my_key = kw0 + l32;
@@ -449,6 +456,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
         dv[off] = to_bf16_bits(dv_acc[dt][r]);
       }
     }
+  }
 }
 
 // ----------------------------------------------------------- B2 (dQ) ----
@@ -670,7 +678,7 @@ void launch_preprocess(const BwdParams& p) {
 template <int D, bool CAUSAL, bool ATOMIC_DQ>
 void launch_kv_outer(const BwdParams& p) {
   const int n_ktiles = (p.N + kBwdKeys - 1) / kBwdKeys;
-  const long long grid = (long long)p.B * p.H * n_ktiles;
+  const long long grid = (long long)p.B * p.H * (CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles);
   const float c = (float)((double)p.scale * 1.4426950408889634);
   hipLaunchKernelGGL((bwd_dl_kernel<D, CAUSAL, ATOMIC_DQ>), dim3((unsigned)grid), dim3(kBwdThreads),
                      0, p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
