@@ -88,6 +88,9 @@ def parse_args():
                         "or fa2_bwd_atomic_dq (fp32 atomics)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--memory", action="store_true",
+                   help="only report the device memory of one forward + backward at "
+                        "N = 4K, 16K, 64K (B=1, H=16, d=128, causal) and exit")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -116,10 +119,62 @@ def calibrate_copy(mib: int) -> None:
                       "ms": round(ms, 4), "GB_per_s": round(2 * n / ms / 1e6, 1)}), flush=True)
 
 
+def activation_memory() -> None:
+    """Device memory of one forward + backward through the library, against
+    what a kernel that materialises the N x N matrices would hold.
+
+    The library allocates nothing: every byte is a caller tensor, so the
+    memory a training step keeps for the backward is O (bf16) and L (fp32),
+    O(N) per head, where standard attention keeps P, O(N^2) per head.  The
+    caller's tensors are allocated with torch and counted exactly; the device's
+    free memory is read around the library calls to show they allocate
+    nothing themselves."""
+    import torch
+
+    from exact_tiled_attention_30_amd import binding
+
+    B, H, d = 1, 16, 128
+    # one small call first: HIP loads the library's code object lazily
+    x = torch.zeros((1, 64, 1, d), dtype=torch.bfloat16, device="cuda")
+    ox, lx = binding.attention_forward(x, x, x, True)
+    binding.attention_backward(x, x, x, ox, lx, x, True)
+    torch.cuda.synchronize()
+    for N in (4096, 16384, 65536):
+        g = torch.Generator(device="cpu").manual_seed(0)
+        q, k, v, do = (torch.randn((B, N, H, d), generator=g).to(torch.bfloat16).cuda()
+                       for _ in range(4))
+        o, lse = torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ws = torch.empty(binding.fa2_bwd_workspace_bytes(B, H, N, d, True), dtype=torch.uint8,
+                         device="cuda")
+        torch.cuda.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        binding.fa2_fwd(q, k, v, o, lse, True, d ** -0.5)
+        binding.fa2_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, True, d ** -0.5)
+        torch.cuda.synchronize()
+        free1 = torch.cuda.mem_get_info()[0]
+        nbytes = lambda *ts: sum(t.numel() * t.element_size() for t in ts)
+        saved = nbytes(o, lse)                     # kept from forward to backward
+        total = nbytes(q, k, v, do, o, lse, dq, dk, dv, ws)
+        std_p = B * H * N * N * 2                  # bf16 P kept for the backward
+        print(json.dumps({
+            "metric": "attention activation memory (fwd+bwd)", "N": N, "B": B, "H": H, "d": d,
+            "causal": True, "saved_for_backward_bytes": saved,
+            "all_tensors_bytes": total, "workspace_bytes": nbytes(ws),
+            "library_allocated_bytes": int(free0 - free1),
+            "standard_attention_P_bytes": std_p,
+            "ratio_standard_over_saved": round(std_p / saved, 1)}), flush=True)
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse_args()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.memory:
+        activation_memory()
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
