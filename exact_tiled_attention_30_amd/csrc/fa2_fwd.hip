@@ -147,6 +147,16 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;
 
+  const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
+  const int n_kv = (kv_len + BC - 1) / BC;
+
+  // The first K/V tiles' DMA goes out before the Q loads, so the two
+  // latencies overlap under the one wait below.
+  if (n_kv > 0) {
+    issue(0, kb0, vb0);
+    if constexpr (STAGES > 2) issue(min(1, n_kv - 1), kb1, vb1);
+  }
+
   bf16x8 qf[D / 16];
   {
     const uint16_t* qp = q + head + (size_t)min(my_q, N - 1) * tok + 8 * hi;
@@ -158,9 +168,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
       qf[cc] = as_bf16x8(x);
     }
   }
-
-  const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
-  const int n_kv = (kv_len + BC - 1) / BC;
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -260,11 +267,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   // newest STAGES-2 batches" -- which leaves tile jt+1 landed.
   static_assert(2 * NIW * (STAGES - 1) <= 15, "vmcnt immediate");
   constexpr int kWaitStep = 0x0F70 | (2 * NIW * (STAGES - 2));
-  if (n_kv > 0) {
-    issue(0, kb0, vb0);
-    if constexpr (STAGES > 2) issue(min(1, n_kv - 1), kb1, vb1);
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitStep);  // tile 0 has landed
+  __builtin_amdgcn_s_waitcnt(kWaitStep);  // tile 0 (and Q) have landed
   __syncthreads();
 
   auto step = [&](int jt, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn)
