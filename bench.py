@@ -83,6 +83,9 @@ def parse_args():
     p.add_argument("--workload", default=None,
                    help="one workload name (default: the N=1024 d=64 pair)")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    p.add_argument("--algo", choices=("fa2", "fa1-order"), default="fa2",
+                   help="forward workloads: fa2_fwd, or the FlashAttention-1-order ablation "
+                        "fa2_fwd_fa1_order")
     p.add_argument("--bwd-dq", choices=("two-pass", "atomic"), default="two-pass",
                    help="dQ strategy of a backward workload: fa2_bwd (a Q-outer dQ pass) "
                         "or fa2_bwd_atomic_dq (fp32 atomics)")
@@ -205,7 +208,15 @@ def main():
 
     launches = []  # (label, callable, flops)
     for w in ws:
-        if not w.backward:
+        if not w.backward and args.algo == "fa1-order":
+            fws = torch.empty(binding.fa2_fwd_fa1_order_workspace_bytes(w.B, w.H, w.N, w.d,
+                                                                        w.causal),
+                              dtype=torch.uint8, device=dev)
+
+            def fwd(w=w, fws=fws):
+                binding.fa2_fwd_fa1_order(x["q"], x["k"], x["v"], o, lse, fws, w.causal, w.scale)
+            launches.append((w.name, fwd, w.flops()))
+        elif not w.backward:
             def fwd(w=w):
                 binding.fa2_fwd(x["q"], x["k"], x["v"], o, lse, w.causal, w.scale)
             launches.append((w.name, fwd, w.flops()))
@@ -289,6 +300,7 @@ def main():
             "causal": [w.causal for w in ws],
             "backward": [w.backward for w in ws],
             **({"bwd_dq": args.bwd_dq} if any(w.backward for w in ws) else {}),
+            **({"algo": args.algo} if args.algo != "fa2" else {}),
             "layout": "[B,N,H,d] bf16 in/out, fp32 lse [B,H,N]",
             "parallelism": "single GPU",
         },

@@ -6,7 +6,8 @@ stream, and turns status codes into exceptions.  There is no fallback: if the
 library is missing the call fails loudly.
 
 Names mirror include/fa2.h: fa2_fwd, fa2_bwd, fa2_bwd_workspace_bytes,
-fa2_bwd_atomic_dq, fa2_bwd_atomic_dq_workspace_bytes, fa2_status_string.
+fa2_bwd_atomic_dq, fa2_bwd_atomic_dq_workspace_bytes, fa2_fwd_fa1_order,
+fa2_fwd_fa1_order_workspace_bytes, fa2_status_string.
 """
 from __future__ import annotations
 
@@ -52,6 +53,11 @@ def lib():
     L.fa2_bwd_atomic_dq_workspace_bytes.restype = ctypes.c_size_t
     L.fa2_bwd_atomic_dq.argtypes = L.fa2_bwd.argtypes
     L.fa2_bwd_atomic_dq.restype = _i
+    L.fa2_fwd_fa1_order_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+    L.fa2_fwd_fa1_order_workspace_bytes.restype = ctypes.c_size_t
+    L.fa2_fwd_fa1_order.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i, _i, _i, _i,
+                                    _i, ctypes.c_float, _vp]
+    L.fa2_fwd_fa1_order.restype = _i
     L.fa2_status_string.argtypes = [_i]
     L.fa2_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -116,6 +122,31 @@ def fa2_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
                          int(bool(causal)), float(scale), _stream(q, stream)))
 
 
+def fa2_fwd_fa1_order_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    return int(lib().fa2_fwd_fa1_order_workspace_bytes(B, H, N, d, int(bool(causal))))
+
+
+def fa2_fwd_fa1_order(q, k, v, o, lse, workspace, causal: bool, scale: float,
+                      stream=None) -> None:
+    """Enqueue the forward pass in FlashAttention-1's loop order (an ablation).
+    workspace: a uint8 device tensor of at least
+    fa2_fwd_fa1_order_workspace_bytes(...) bytes.  Raises Fa2Error."""
+    import torch
+
+    B, N, H, d = _bnhd(q)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _require(t, torch.bfloat16, name)
+        if tuple(t.shape) != (B, N, H, d):
+            raise ValueError(f"{name} must have shape {(B, N, H, d)}")
+    _require(lse, torch.float32, "lse")
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"lse must have shape {(B, H, N)}")
+    _require(workspace, torch.uint8, "workspace")
+    _check(lib().fa2_fwd_fa1_order(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                                   workspace.numel(), B, H, N, d, int(bool(causal)), float(scale),
+                                   _stream(q, stream)))
+
+
 def fa2_bwd_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
     return int(lib().fa2_bwd_workspace_bytes(B, H, N, d, int(bool(causal))))
 
@@ -168,6 +199,21 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa2_fwd(q, k, v, o, lse, causal, scale)
+    return o, lse
+
+
+def attention_forward_fa1_order(q, k, v, causal: bool = False, scale: float | None = None):
+    """Allocate O, L and the workspace, run fa2_fwd_fa1_order, return (o, lse)."""
+    import torch
+
+    B, N, H, d = _bnhd(q)
+    if scale is None:
+        scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(1, fa2_fwd_fa1_order_workspace_bytes(B, H, N, d, causal)),
+                     dtype=torch.uint8, device=q.device)
+    fa2_fwd_fa1_order(q, k, v, o, lse, ws, causal, scale)
     return o, lse
 
 

@@ -53,6 +53,7 @@ size_t bwd_delta_bytes(int B, int H, int N) { return align256((size_t)B * H * N 
 size_t bwd_dq_acc_bytes(int B, int H, int N, int d) {
   return align256((size_t)B * H * N * d * sizeof(float));
 }
+size_t fa1_ml_bytes(int B, int H, int N) { return align256((size_t)B * H * N * 2 * sizeof(float)); }
 }  // namespace fa2
 
 extern "C" {
@@ -92,6 +93,42 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
 
   fa2::FwdParams p{q, k, v, o, lse, B, H, N, d, causal != 0, scale, (hipStream_t)stream};
   return fa2::launch_fwd(p) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+size_t fa2_fwd_fa1_order_workspace_bytes(int B, int H, int N, int d, int causal) {
+  (void)causal;
+  size_t elems = 0, rows = 0;
+  if (check_shape(B, H, N, d, 1.0f, &elems, &rows) != FA2_OK || elems == 0) return 0;
+  return fa2::bwd_dq_acc_bytes(B, H, N, d) + fa2::fa1_ml_bytes(B, H, N);
+}
+
+int fa2_fwd_fa1_order(const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                      int causal, float scale, void* stream) {
+  size_t elems = 0, rows = 0;
+  const int st = check_shape(B, H, N, d, scale, &elems, &rows);
+  if (st != FA2_OK) return st;
+  if (elems == 0) return FA2_OK;
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_NULLPTR;
+  if (!workspace || workspace_bytes < fa2_fwd_fa1_order_workspace_bytes(B, H, N, d, causal))
+    return FA2_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 16))
+    return FA2_ERR_ALIGN;
+  const size_t tb = elems * 2, lb = rows * sizeof(float);
+  const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const Range outs[] = {range_of(o, tb), range_of(lse, lb), range_of(workspace, workspace_bytes)};
+  for (const Range& out : outs)
+    for (const Range& in : ins)
+      if (overlap(out, in)) return FA2_ERR_ALIAS;
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return FA2_ERR_ALIAS;
+  char* ws = (char*)workspace;
+  fa2::Fa1Params p{q, k, v, o, lse, (float*)ws,
+                   (float*)(ws + fa2::bwd_dq_acc_bytes(B, H, N, d)), B, H, N, d, causal != 0,
+                   scale, (hipStream_t)stream};
+  return fa2::launch_fa1_order_fwd(p) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d, int causal) {

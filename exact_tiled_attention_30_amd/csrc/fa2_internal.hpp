@@ -37,11 +37,28 @@ struct BwdParams {
   hipStream_t stream;
 };
 
+// The forward pass in FlashAttention-1's loop order (an ablation).
+struct Fa1Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* o_state;   // fp32 [B, N, H, d] (workspace)
+  float* ml_state;  // fp32 [B, H, N, 2]: running max, running sum (workspace)
+  int B, H, N, d;
+  bool causal;
+  float scale;
+  hipStream_t stream;
+};
+
 // Workspace layout of the backward pass (offsets in bytes, 256-aligned).
 size_t bwd_delta_bytes(int B, int H, int N);
 size_t bwd_dq_acc_bytes(int B, int H, int N, int d);
+size_t fa1_ml_bytes(int B, int H, int N);
 
 hipError_t launch_fwd(const FwdParams& p);
+hipError_t launch_fa1_order_fwd(const Fa1Params& p);
 hipError_t launch_bwd(const BwdParams& p);             // dQ from a Q-outer pass
 hipError_t launch_bwd_atomic_dq(const BwdParams& p);   // dQ summed with fp32 atomics
 

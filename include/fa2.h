@@ -120,6 +120,30 @@ int fa2_bwd_atomic_dq(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                       int causal, float scale, void* stream);
 
+/*
+ * Bytes of device workspace fa2_fwd_fa1_order needs (0 if the problem is
+ * empty or the arguments are invalid): the fp32 O state ([B, N, H, d]) and
+ * the running max and sum of every row (fp32 [B, H, N, 2]), each 256-byte
+ * aligned.
+ */
+size_t fa2_fwd_fa1_order_workspace_bytes(int B, int H, int N, int d, int causal);
+
+/*
+ * The forward pass in FlashAttention-1's loop order, kept to measure what
+ * FlashAttention-2's changes buy ("FlashAttention Implementation >
+ * FlashAttention-2 Improvements"; "6.2 FlashAttention V2 in depth", sections
+ * 2.1 and 3.1-3.3): K/V tiles in the outer loop and Q tiles in the inner
+ * one, the Q tile reloaded and the O tile and its row statistics read and
+ * written back (in the fp32 workspace) at every step, O renormalised after
+ * every step, and one workgroup per (batch, head).  Same inputs, outputs,
+ * layouts, ownership and errors as fa2_fwd, plus the workspace (at least
+ * fa2_fwd_fa1_order_workspace_bytes() bytes, 16-byte aligned, contents on
+ * entry ignored and overwritten).
+ */
+int fa2_fwd_fa1_order(const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                      int causal, float scale, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa2_status_string(int status);
 

@@ -32,13 +32,14 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa2_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa2_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa2_bwd", "fa2_bwd_atomic_dq",
                                     "fa2_bwd_atomic_dq_workspace_bytes",
-                                    "fa2_bwd_workspace_bytes", "fa2_fwd", "fa2_status_string"]
+                                    "fa2_bwd_workspace_bytes", "fa2_fwd", "fa2_fwd_fa1_order",
+                                    "fa2_fwd_fa1_order_workspace_bytes", "fa2_status_string"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -138,3 +139,28 @@ def test_atomic_workspace_is_larger(L):
     # the two-pass backward's workspace is too small for the atomic one
     need = L.fa2_bwd_workspace_bytes(2, 3, 100, 64, 1)
     assert bwd(L, ws_bytes=need, atomic=True) == WORKSPACE
+
+
+def fa1(L, q=Q, k=K, v=V, o=O, lse=LSE, ws=WS, ws_bytes=None, B=2, H=3, N=100, d=64, causal=0,
+        scale=0.125):
+    if ws_bytes is None:
+        ws_bytes = L.fa2_fwd_fa1_order_workspace_bytes(B, H, N, d, causal)
+    return L.fa2_fwd_fa1_order(q, k, v, o, lse, ws, ws_bytes, B, H, N, d, causal,
+                               ctypes.c_float(scale), None)
+
+
+def test_fa1_order_argument_errors(L):
+    B, H, N, d = 2, 3, 100, 64
+    want = ((B * N * H * d * 4 + 255) // 256 * 256) + ((B * H * N * 8 + 255) // 256 * 256)
+    assert L.fa2_fwd_fa1_order_workspace_bytes(B, H, N, d, 0) == want
+    assert L.fa2_fwd_fa1_order_workspace_bytes(B, H, N, 80, 0) == 0
+    assert fa1(L, d=96) == HEADDIM
+    assert fa1(L, N=-1) == SHAPE
+    assert fa1(L, scale=math.nan) == SCALE
+    assert fa1(L, q=None) == NULLPTR
+    assert fa1(L, ws=None) == WORKSPACE
+    assert fa1(L, ws_bytes=want - 1) == WORKSPACE
+    assert fa1(L, o=O + 2) == ALIGN
+    assert fa1(L, ws=Q) == ALIAS
+    assert fa1(L, o=K) == ALIAS
+    assert fa1(L, N=0, q=None, ws=None) == OK

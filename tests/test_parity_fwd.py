@@ -155,3 +155,35 @@ def test_causal_wide_grid_ragged(d):
     rep = forward_report(o[b, i, h].cpu(), lse[b, h, i].cpu(), o_ref, lse_ref)
     print(f"  {rep}", flush=True)
     assert rep["ok"], rep
+
+
+# ---- the FlashAttention-1-order ablation (fa2_fwd_fa1_order) -------------
+
+FA1_SHAPES = [(1, 1, 128, 64), (2, 3, 200, 64), (1, 2, 333, 128), (1, 1, 1000, 64),
+              (1, 1, 1, 128), (2, 2, 520, 128)]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", FA1_SHAPES, ids=lambda s: "b{}h{}n{}d{}".format(*s))
+def test_fa1_order_every_element(shape, causal):
+    B, H, N, d = shape
+    x = make_inputs(B, H, N, d, seed=17)
+    print(f"[fa1-order] shape={shape} causal={causal}", flush=True)
+    dx = _dev(x)
+    o, lse = binding.attention_forward_fa1_order(dx["q"], dx["k"], dx["v"], causal, d ** -0.5)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal, d ** -0.5)
+    rep = forward_report(o.cpu(), lse.cpu(), o_ref, lse_ref)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125])
+def test_fa1_order_unusual_scales(scale):
+    B, H, N, d = 1, 2, 300, 64
+    x = make_inputs(B, H, N, d, seed=5)
+    dx = _dev(x)
+    o, lse = binding.attention_forward_fa1_order(dx["q"], dx["k"], dx["v"], True, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], True, scale)
+    rep = forward_report(o.cpu(), lse.cpu(), o_ref, lse_ref)
+    assert rep["ok"], rep
