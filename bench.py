@@ -83,9 +83,9 @@ def parse_args():
     p.add_argument("--workload", default=None,
                    help="one workload name (default: the N=1024 d=64 pair)")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    p.add_argument("--algo", choices=("fa2", "fa1-order"), default="fa2",
-                   help="forward workloads: fa2_fwd, or the FlashAttention-1-order ablation "
-                        "fa2_fwd_fa1_order")
+    p.add_argument("--algo", choices=("fa2", "split-kv", "fa1-order"), default="fa2",
+                   help="forward workloads: fa2_fwd, fa2_fwd_split_kv (library's slice "
+                        "count), or the FlashAttention-1-order ablation fa2_fwd_fa1_order")
     p.add_argument("--bwd-dq", choices=("two-pass", "atomic"), default="two-pass",
                    help="dQ strategy of a backward workload: fa2_bwd (a Q-outer dQ pass) "
                         "or fa2_bwd_atomic_dq (fp32 atomics)")
@@ -208,7 +208,15 @@ def main():
 
     launches = []  # (label, callable, flops)
     for w in ws:
-        if not w.backward and args.algo == "fa1-order":
+        if not w.backward and args.algo == "split-kv":
+            sws = torch.empty(binding.fa2_fwd_split_kv_workspace_bytes(w.B, w.H, w.N, w.d,
+                                                                       w.causal, 0),
+                              dtype=torch.uint8, device=dev)
+
+            def fwd(w=w, sws=sws):
+                binding.fa2_fwd_split_kv(x["q"], x["k"], x["v"], o, lse, sws, w.causal, w.scale, 0)
+            launches.append((w.name, fwd, w.flops()))
+        elif not w.backward and args.algo == "fa1-order":
             fws = torch.empty(binding.fa2_fwd_fa1_order_workspace_bytes(w.B, w.H, w.N, w.d,
                                                                         w.causal),
                               dtype=torch.uint8, device=dev)

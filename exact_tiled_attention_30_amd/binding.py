@@ -6,8 +6,9 @@ stream, and turns status codes into exceptions.  There is no fallback: if the
 library is missing the call fails loudly.
 
 Names mirror include/fa2.h: fa2_fwd, fa2_bwd, fa2_bwd_workspace_bytes,
-fa2_bwd_atomic_dq, fa2_bwd_atomic_dq_workspace_bytes, fa2_fwd_fa1_order,
-fa2_fwd_fa1_order_workspace_bytes, fa2_status_string.
+fa2_bwd_atomic_dq, fa2_bwd_atomic_dq_workspace_bytes, fa2_fwd_split_kv,
+fa2_fwd_split_kv_workspace_bytes, fa2_fwd_fa1_order, fa2_fwd_fa1_order_workspace_bytes,
+fa2_status_string.
 """
 from __future__ import annotations
 
@@ -53,6 +54,11 @@ def lib():
     L.fa2_bwd_atomic_dq_workspace_bytes.restype = ctypes.c_size_t
     L.fa2_bwd_atomic_dq.argtypes = L.fa2_bwd.argtypes
     L.fa2_bwd_atomic_dq.restype = _i
+    L.fa2_fwd_split_kv_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+    L.fa2_fwd_split_kv_workspace_bytes.restype = ctypes.c_size_t
+    L.fa2_fwd_split_kv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i, _i, _i, _i,
+                                   _i, ctypes.c_float, _i, _vp]
+    L.fa2_fwd_split_kv.restype = _i
     L.fa2_fwd_fa1_order_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
     L.fa2_fwd_fa1_order_workspace_bytes.restype = ctypes.c_size_t
     L.fa2_fwd_fa1_order.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i, _i, _i, _i,
@@ -120,6 +126,32 @@ def fa2_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
         raise ValueError(f"lse must have shape {(B, H, N)}")
     _check(lib().fa2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                          int(bool(causal)), float(scale), _stream(q, stream)))
+
+
+def fa2_fwd_split_kv_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool,
+                                     n_split: int = 0) -> int:
+    return int(lib().fa2_fwd_split_kv_workspace_bytes(B, H, N, d, int(bool(causal)),
+                                                       int(n_split)))
+
+
+def fa2_fwd_split_kv(q, k, v, o, lse, workspace, causal: bool, scale: float, n_split: int = 0,
+                     stream=None) -> None:
+    """Enqueue the split-KV forward pass.  workspace: a uint8 device tensor of
+    at least fa2_fwd_split_kv_workspace_bytes(..., n_split) bytes.  Raises Fa2Error."""
+    import torch
+
+    B, N, H, d = _bnhd(q)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _require(t, torch.bfloat16, name)
+        if tuple(t.shape) != (B, N, H, d):
+            raise ValueError(f"{name} must have shape {(B, N, H, d)}")
+    _require(lse, torch.float32, "lse")
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"lse must have shape {(B, H, N)}")
+    _require(workspace, torch.uint8, "workspace")
+    _check(lib().fa2_fwd_split_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                                  workspace.numel(), B, H, N, d, int(bool(causal)), float(scale),
+                                  int(n_split), _stream(q, stream)))
 
 
 def fa2_fwd_fa1_order_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
@@ -199,6 +231,22 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa2_fwd(q, k, v, o, lse, causal, scale)
+    return o, lse
+
+
+def attention_forward_split_kv(q, k, v, causal: bool = False, scale: float | None = None,
+                               n_split: int = 0):
+    """Allocate O, L and the workspace, run fa2_fwd_split_kv, return (o, lse)."""
+    import torch
+
+    B, N, H, d = _bnhd(q)
+    if scale is None:
+        scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(1, fa2_fwd_split_kv_workspace_bytes(B, H, N, d, causal, n_split)),
+                     dtype=torch.uint8, device=q.device)
+    fa2_fwd_split_kv(q, k, v, o, lse, ws, causal, scale, n_split)
     return o, lse
 
 

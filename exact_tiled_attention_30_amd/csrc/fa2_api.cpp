@@ -13,6 +13,7 @@
 namespace {
 
 constexpr size_t kMaxElems = (size_t)1 << 62;
+constexpr int kMaxSplits = 64;  // split-KV slices per Q tile
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -93,6 +94,48 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
 
   fa2::FwdParams p{q, k, v, o, lse, B, H, N, d, causal != 0, scale, (hipStream_t)stream};
   return fa2::launch_fwd(p) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+size_t fa2_fwd_split_kv_workspace_bytes(int B, int H, int N, int d, int causal, int n_split) {
+  (void)causal;
+  size_t elems = 0, rows = 0;
+  if (check_shape(B, H, N, d, 1.0f, &elems, &rows) != FA2_OK || elems == 0) return 0;
+  if (n_split > kMaxSplits) return 0;
+  const size_t s = (size_t)fa2::split_kv_slices(B, H, N, n_split);
+  return s * (align256(elems * sizeof(float)) + align256(rows * sizeof(float)));
+}
+
+int fa2_fwd_split_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                     int causal, float scale, int n_split, void* stream) {
+  size_t elems = 0, rows = 0;
+  const int st = check_shape(B, H, N, d, scale, &elems, &rows);
+  if (st != FA2_OK) return st;
+  if (n_split > kMaxSplits) return FA2_ERR_SHAPE;
+  if (elems == 0) return FA2_OK;
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_NULLPTR;
+  if (!workspace ||
+      workspace_bytes < fa2_fwd_split_kv_workspace_bytes(B, H, N, d, causal, n_split))
+    return FA2_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 16))
+    return FA2_ERR_ALIGN;
+  const size_t tb = elems * 2, lb = rows * sizeof(float);
+  const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const Range outs[] = {range_of(o, tb), range_of(lse, lb), range_of(workspace, workspace_bytes)};
+  for (const Range& out : outs)
+    for (const Range& in : ins)
+      if (overlap(out, in)) return FA2_ERR_ALIAS;
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return FA2_ERR_ALIAS;
+  const int s = fa2::split_kv_slices(B, H, N, n_split);
+  char* ws = (char*)workspace;
+  fa2::FwdParams p{q, k, v, o, lse, B, H, N, d, causal != 0, scale, (hipStream_t)stream};
+  p.n_split = s;
+  p.o_part = (float*)ws;
+  p.lse_part = (float*)(ws + (size_t)s * align256(elems * sizeof(float)));
+  return fa2::launch_fwd_split_kv(p) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
 size_t fa2_fwd_fa1_order_workspace_bytes(int B, int H, int N, int d, int causal) {

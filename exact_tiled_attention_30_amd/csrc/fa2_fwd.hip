@@ -66,11 +66,15 @@ struct DlSwz {
   __device__ static constexpr int v(int r) { return D == 128 ? 4 * (r % 4) : 4 * ((r / 2) % 2); }
 };
 
-template <int D, int BC, int W, int STAGES, bool CAUSAL>
+// SPLIT: the key range of every Q tile is cut into n_split slices, one work
+// item each; a slice's normalised O (fp32) and its logsumexp (log2 units) go
+// to o_part / lse_part, and fwd_combine_kernel merges them.
+template <int D, int BC, int W, int STAGES, bool CAUSAL, bool SPLIT = false>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 1))) void fwd_dl_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int H, int N, int n_qtiles, int grid, float c, uint32_t q_and, uint32_t q_xor) {
+    int H, int N, int n_qtiles, int grid, float c, uint32_t q_and, uint32_t q_xor,
+    int n_split = 1, float* __restrict__ o_part = nullptr, float* __restrict__ lse_part = nullptr) {
   constexpr int kWaves = W;
   constexpr int BR = kWaves * 32;
   constexpr int RB = D * 2;                 // bytes per LDS row
@@ -96,11 +100,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   // Work item: non-causal, one Q tile; causal, the pair (n_qtiles-1-p, p)
   // of a heavy and a light Q tile, so every workgroup streams the same
   // number of K/V tiles (n_qtiles + 1 tile rows of keys) whatever p is.
-  const int logical = xcd_contiguous_id(blockIdx.x, grid);
-  const int per_head = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+  const int logical0 = xcd_contiguous_id(blockIdx.x, grid);
+  const int split = SPLIT ? logical0 % n_split : 0;  // slices of one Q tile are adjacent
+  const int logical = SPLIT ? logical0 / n_split : logical0;
+  const int per_head = (CAUSAL && !SPLIT) ? (n_qtiles + 1) / 2 : n_qtiles;
   const int bh = logical / per_head;
   const int item = logical % per_head;
-  const int n_pass = (CAUSAL && item != n_qtiles - 1 - item) ? 2 : 1;
+  const int n_pass = (CAUSAL && !SPLIT && item != n_qtiles - 1 - item) ? 2 : 1;
   const int b = bh / H, hh = bh % H;
   const size_t tok = (size_t)H * D;
   const size_t head = (size_t)b * N * tok + (size_t)hh * D;
@@ -142,19 +148,23 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   };
 
   for (int pass = 0; pass < n_pass; ++pass) {
-  const int qt = CAUSAL ? (pass == 0 ? n_qtiles - 1 - item : item) : item;
+  const int qt = (CAUSAL && !SPLIT) ? (pass == 0 ? n_qtiles - 1 - item : item) : item;
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;
 
   const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
-  const int n_kv = (kv_len + BC - 1) / BC;
+  const int n_kv_all = (kv_len + BC - 1) / BC;
+  // this work item's K/V tiles: [jt_begin, n_kv)
+  const int chunk = SPLIT ? (n_kv_all + n_split - 1) / n_split : n_kv_all;
+  const int jt_begin = SPLIT ? min(n_kv_all, split * chunk) : 0;
+  const int n_kv = SPLIT ? min(n_kv_all, jt_begin + chunk) : n_kv_all;
 
   // The first K/V tiles' DMA goes out before the Q loads, so the two
   // latencies overlap under the one wait below.
-  if (n_kv > 0) {
-    issue(0, kb0, vb0);
-    if constexpr (STAGES > 2) issue(min(1, n_kv - 1), kb1, vb1);
+  if (n_kv > jt_begin) {
+    issue(jt_begin, kb0, vb0);
+    if constexpr (STAGES > 2) issue(min(jt_begin + 1, n_kv - 1), kb1, vb1);
   }
 
   bf16x8 qf[D / 16];
@@ -278,13 +288,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
     __syncthreads();
   };
   if constexpr (STAGES == 3) {
-    for (int jt = 0; jt < n_kv; jt += 3) {
+    for (int jt = jt_begin; jt < n_kv; jt += 3) {
       step(jt, kb0, vb0, kb2, vb2);
       if (jt + 1 < n_kv) step(jt + 1, kb1, vb1, kb0, vb0);
       if (jt + 2 < n_kv) step(jt + 2, kb2, vb2, kb1, vb1);
     }
   } else {
-    for (int jt = 0; jt < n_kv; jt += 2) {
+    for (int jt = jt_begin; jt < n_kv; jt += 2) {
       step(jt, kb0, vb0, kb1, vb1);
       if (jt + 1 < n_kv) step(jt + 1, kb1, vb1, kb0, vb0);
     }
@@ -292,6 +302,26 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   __builtin_amdgcn_s_waitcnt(0x0F70);  // drain the LDS DMA before exit
 
   const float l = pair_sum(l_part);
+  if constexpr (SPLIT) {
+    // partial result of this slice: O / l in fp32 and log2(sum) + m; a
+    // slice with no visible key for a row has l == 0, so it writes O = 0 and
+    // -inf, which weighs nothing in the merge
+    if (my_q < N) {
+      const size_t rows_all = (size_t)(grid / n_split / per_head) * (size_t)N;  // B * H * N
+      float* opp = o_part + (size_t)split * rows_all * D + head + (size_t)my_q * tok;
+      const float inv_p = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(f32x4*)(opp + dt * 32 + 8 * g + 4 * hi) =
+              f32x4{oacc[dt][4 * g + 0], oacc[dt][4 * g + 1], oacc[dt][4 * g + 2],
+                    oacc[dt][4 * g + 3]} * inv_p;
+      if (hi == 0)
+        lse_part[(size_t)split * rows_all + ((size_t)b * H + hh) * N + my_q] =
+            l > 0.f ? m_run + log2f(l) : -INFINITY;
+    }
+  } else {
   const float inv = 1.0f / l;
   if (my_q < N) {
     uint16_t* op = o + head + (size_t)my_q * tok;
@@ -304,6 +334,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
         *(u32x2*)(op + dt * 32 + 8 * g + 4 * hi) = __builtin_bit_cast(u32x2, to_bf16x4(x));
       }
     if (hi == 0) lse[((size_t)b * H + hh) * N + my_q] = (m_run + log2f(l)) * kLn2;
+  }
   }
   if (pass + 1 < n_pass) __syncthreads();  // every wave is done with the LDS tiles
   }
@@ -326,6 +357,63 @@ hipError_t launch_fwd_dl(const FwdParams& p) {
   return hipGetLastError();
 }
 
+// Split-KV merge: for every row, L = log2 sum_s 2^{L_s} and
+// O = sum_s 2^{L_s - L} O_s, i.e. the slices' softmax sums re-weighted to the
+// whole key range (each O_s was normalised by its own sum).  One thread per
+// 8 consecutive elements of a row; rows in [B, N, H] order.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restrict__ o_part,
+                                                          const float* __restrict__ lse_part,
+                                                          uint16_t* __restrict__ o,
+                                                          float* __restrict__ lse, int H, int N,
+                                                          long long rows, int n_split) {
+  constexpr int CH = D / 8;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = t / CH;
+  const int ch = (int)(t % CH);
+  if (row >= rows) return;
+  const long long h = row % H, n = (row / H) % N, b = row / ((long long)H * N);
+  const size_t li = ((size_t)b * H + h) * N + n;
+  float m = -INFINITY;
+  for (int sl = 0; sl < n_split; ++sl) m = fmaxf(m, lse_part[(size_t)sl * rows + li]);
+  f32x8 acc = f32x8{};
+  float wsum = 0.f;
+  for (int sl = 0; sl < n_split; ++sl) {
+    const float ls = lse_part[(size_t)sl * rows + li];
+    const float w = (ls == -INFINITY) ? 0.f : fast_exp2(ls - m);
+    wsum += w;
+    const float* src = o_part + ((size_t)sl * rows + row) * D + ch * 8;
+    const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+    acc += w * f32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  }
+  const float inv = 1.0f / wsum;
+  *(u32x4*)(o + row * D + ch * 8) = as_u32x4(to_bf16x8(acc * inv));
+  if (ch == 0) lse[li] = (m + log2f(wsum)) * kLn2;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_split_t(const FwdParams& p) {
+  constexpr int W = 4, BR = W * 32;
+  const int n_qtiles = (p.N + BR - 1) / BR;
+  const long long grid = (long long)p.B * p.H * n_qtiles * p.n_split;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
+  const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
+  const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((fwd_dl_kernel<D, 64, W, 2, CAUSAL, true>), dim3((unsigned)grid), dim3(W * 64),
+                     0, p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
+                     (uint16_t*)p.o, p.lse, p.H, p.N, n_qtiles, (int)grid, c, q_and, q_xor,
+                     p.n_split, p.o_part, p.lse_part);
+  const long long rows = (long long)p.B * p.N * p.H;
+  const long long threads = rows * (D / 8);
+  hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     p.stream, p.o_part, p.lse_part, (uint16_t*)p.o, p.lse, p.H, p.N, rows,
+                     p.n_split);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p) {
@@ -342,6 +430,24 @@ hipError_t launch_fwd(const FwdParams& p) {
     return small ? launch_fwd_dl<64, 64, 4, 2, true>(p) : launch_fwd_dl<64, 64, 8, 2, true>(p);
   }
   return small ? launch_fwd_dl<128, 64, 4, 2, true>(p) : launch_fwd_dl<128, 64, 8, 2, true>(p);
+}
+
+int split_kv_slices(int B, int H, int N, int requested) {
+  if (requested > 0) return requested;
+  // enough work items for two 4-wave workgroups per CU, at most 16 slices,
+  // and at least two 64-key tiles per slice
+  constexpr long long kCus = 256;
+  const long long items = (long long)B * H * ((N + 127) / 128);
+  long long s = (2 * kCus + items - 1) / items;
+  const long long max_by_keys = ((N + 63) / 64) / 2;
+  s = s < 16 ? s : 16;
+  s = s < max_by_keys ? s : max_by_keys;
+  return (int)(s < 1 ? 1 : s);
+}
+
+hipError_t launch_fwd_split_kv(const FwdParams& p) {
+  if (p.d == 64) return p.causal ? launch_split_t<64, true>(p) : launch_split_t<64, false>(p);
+  return p.causal ? launch_split_t<128, true>(p) : launch_split_t<128, false>(p);
 }
 
 }  // namespace fa2

@@ -17,6 +17,10 @@ struct FwdParams {
   bool causal;
   float scale;
   hipStream_t stream;
+  // split-KV only (launch_fwd_split_kv): slices per Q tile and the partials
+  int n_split = 1;
+  float* o_part = nullptr;    // fp32 [n_split][B, N, H, d] (workspace)
+  float* lse_part = nullptr;  // fp32 [n_split][B, H, N], log2 units (workspace)
 };
 
 struct BwdParams {
@@ -58,6 +62,8 @@ size_t bwd_dq_acc_bytes(int B, int H, int N, int d);
 size_t fa1_ml_bytes(int B, int H, int N);
 
 hipError_t launch_fwd(const FwdParams& p);
+hipError_t launch_fwd_split_kv(const FwdParams& p);
+int split_kv_slices(int B, int H, int N, int requested);
 hipError_t launch_fa1_order_fwd(const Fa1Params& p);
 hipError_t launch_bwd(const BwdParams& p);             // dQ from a Q-outer pass
 hipError_t launch_bwd_atomic_dq(const BwdParams& p);   // dQ summed with fp32 atomics

@@ -103,4 +103,7 @@ WORKLOADS = {w.name: w for w in [
     Workload("fwd_b1_h16_n32768_d128_causal_peaked", 1, 16, 32768, 128, True,
              peaked_fraction=0.01),
     Workload("bwd_b4_h16_n4096_d128_causal", 4, 16, 4096, 128, True, backward=True),
+    # few heads, long sequence: B*H*ceil(N/256) = 128 workgroups cannot fill
+    # 256 CUs (the case split-KV is for)
+    Workload("fwd_b1_h2_n16384_d128_full", 1, 2, 16384, 128, False),
 ]}

@@ -121,6 +121,33 @@ int fa2_bwd_atomic_dq(const void* q, const void* k, const void* v, const void* o
                       int causal, float scale, void* stream);
 
 /*
+ * Bytes of device workspace fa2_fwd_split_kv needs for these sizes and
+ * n_split (0 if the problem is empty or the arguments are invalid): per
+ * slice, an fp32 partial O ([B, N, H, d]) and an fp32 partial logsumexp
+ * ([B, H, N]).  n_split <= 0 asks for the library's choice, the same one
+ * fa2_fwd_split_kv makes.
+ */
+size_t fa2_fwd_split_kv_workspace_bytes(int B, int H, int N, int d, int causal, int n_split);
+
+/*
+ * The forward pass with the key range of every Q tile cut into n_split
+ * slices that run as separate workgroups, for problems whose
+ * B * H * ceil(N / 128) workgroups cannot fill the GPU ("FlashAttention
+ * Implementation > FlashAttention-2 Improvements", "Better Work
+ * Partitioning": work split across blocks even for a single head).  Each
+ * slice leaves its normalised partial O and logsumexp in the workspace; a
+ * second kernel merges them with logsumexp weights into O and L.  Inputs,
+ * outputs, layouts and errors as for fa2_fwd; n_split <= 0 lets the library
+ * choose (enough work items for the GPU, at most 16, at least two 64-key
+ * tiles per slice), n_split > 64 is FA2_ERR_SHAPE.  workspace: at least
+ * fa2_fwd_split_kv_workspace_bytes() bytes for the same n_split, 16-byte
+ * aligned, contents on entry ignored and overwritten.
+ */
+int fa2_fwd_split_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                     int causal, float scale, int n_split, void* stream);
+
+/*
  * Bytes of device workspace fa2_fwd_fa1_order needs (0 if the problem is
  * empty or the arguments are invalid): the fp32 O state ([B, N, H, d]) and
  * the running max and sum of every row (fp32 [B, H, N, 2]), each 256-byte

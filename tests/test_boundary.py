@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == ["fa2_bwd", "fa2_bwd_atomic_dq",
                                     "fa2_bwd_atomic_dq_workspace_bytes",
                                     "fa2_bwd_workspace_bytes", "fa2_fwd", "fa2_fwd_fa1_order",
-                                    "fa2_fwd_fa1_order_workspace_bytes", "fa2_status_string"]
+                                    "fa2_fwd_fa1_order_workspace_bytes", "fa2_fwd_split_kv",
+                                    "fa2_fwd_split_kv_workspace_bytes", "fa2_status_string"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -164,3 +165,28 @@ def test_fa1_order_argument_errors(L):
     assert fa1(L, ws=Q) == ALIAS
     assert fa1(L, o=K) == ALIAS
     assert fa1(L, N=0, q=None, ws=None) == OK
+
+
+def split(L, q=Q, k=K, v=V, o=O, lse=LSE, ws=WS, ws_bytes=None, B=2, H=3, N=1000, d=64, causal=0,
+          scale=0.125, n_split=0):
+    if ws_bytes is None:
+        ws_bytes = L.fa2_fwd_split_kv_workspace_bytes(B, H, N, d, causal, n_split)
+    return L.fa2_fwd_split_kv(q, k, v, o, lse, ws, ws_bytes, B, H, N, d, causal,
+                              ctypes.c_float(scale), n_split, None)
+
+
+def test_split_kv_argument_errors(L):
+    B, H, N, d = 2, 3, 1000, 64
+    per = ((B * N * H * d * 4 + 255) // 256 * 256) + ((B * H * N * 4 + 255) // 256 * 256)
+    assert L.fa2_fwd_split_kv_workspace_bytes(B, H, N, d, 0, 3) == 3 * per
+    auto = L.fa2_fwd_split_kv_workspace_bytes(B, H, N, d, 0, 0)
+    assert auto % per == 0 and 1 <= auto // per <= 16
+    assert L.fa2_fwd_split_kv_workspace_bytes(B, H, N, d, 0, 65) == 0
+    assert split(L, n_split=65) == SHAPE
+    assert split(L, d=80) == HEADDIM
+    assert split(L, ws=None) == WORKSPACE
+    assert split(L, n_split=4, ws_bytes=4 * per - 1) == WORKSPACE
+    assert split(L, lse=None) == NULLPTR
+    assert split(L, ws=V) == ALIAS
+    assert split(L, q=Q + 8) == ALIGN
+    assert split(L, N=0, q=None, ws=None) == OK

@@ -187,3 +187,24 @@ def test_fa1_order_unusual_scales(scale):
     o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], True, scale)
     rep = forward_report(o.cpu(), lse.cpu(), o_ref, lse_ref)
     assert rep["ok"], rep
+
+
+# ---- split-KV (fa2_fwd_split_kv) ------------------------------------------
+
+SPLIT_CASES = [((1, 1, 1000, 64), 3), ((2, 2, 200, 128), 5), ((1, 2, 777, 128), 2),
+               ((1, 1, 4096, 64), 0), ((1, 1, 64, 64), 4), ((2, 1, 1500, 128), 0)]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "b{}h{}n{}d{}-s{}".format(*c[0], c[1]))
+def test_split_kv_every_element(case, causal):
+    (B, H, N, d), n_split = case
+    x = make_inputs(B, H, N, d, seed=19)
+    print(f"[split-kv] shape={(B, H, N, d)} n_split={n_split} causal={causal}", flush=True)
+    dx = _dev(x)
+    o, lse = binding.attention_forward_split_kv(dx["q"], dx["k"], dx["v"], causal, d ** -0.5,
+                                                n_split)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal, d ** -0.5)
+    rep = forward_report(o.cpu(), lse.cpu(), o_ref, lse_ref)
+    assert rep["ok"], rep
