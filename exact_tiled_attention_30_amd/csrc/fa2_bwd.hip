@@ -482,8 +482,8 @@ template <int D, int W, bool CAUSAL>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W))) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dq,
-    int H, int N, int n_qtiles, int grid, float c, float scale) {
+    const uint16_t* __restrict__ o, const float* __restrict__ lse, float* __restrict__ delta,
+    uint16_t* __restrict__ dq, int H, int N, int n_qtiles, int grid, float c, float scale) {
   constexpr int BC = 64;                    // keys per K/V tile
   constexpr int BR = W * 32;                // query rows per Q tile
   constexpr int RB = D * 2;
@@ -574,7 +574,26 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
       }
     }
     const float l2 = lse[rowstat + qc] * kLog2e;
-    const float dd = delta[rowstat + qc];
+    // D_i = rowsum(dO_i * O_i) (section 7.3), computed here from the rows
+    // this wave already holds and written once for the KV-outer pass: the
+    // two lane halves hold the two halves of the row
+    float dd;
+    {
+      const uint16_t* op = o + head + (size_t)qc * tok + 8 * hi;
+      float part = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) {
+        const u32x4 ox = *(const u32x4*)(op + 16 * cc);
+        const u32x4 gx = as_u32x4(dof[cc]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          part += __uint_as_float(ox[t] << 16) * __uint_as_float(gx[t] << 16);
+          part += __uint_as_float(ox[t] & 0xffff0000u) * __uint_as_float(gx[t] & 0xffff0000u);
+        }
+      }
+      dd = pair_sum(part);
+      if (my_q < N && hi == 0) delta[rowstat + my_q] = dd;
+    }
 
     const int kv_len = CAUSAL ? min(N, q0 + BR) : N;
     const int n_kv = (kv_len + BC - 1) / BC;
@@ -694,8 +713,8 @@ void launch_dq_pass(const BwdParams& p) {
   const float c = (float)((double)p.scale * 1.4426950408889634);
   hipLaunchKernelGGL((bwd_dq_kernel<D, W, CAUSAL>), dim3((unsigned)grid), dim3(W * 64), 0, p.stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
-                     (const uint16_t*)p.dout, p.lse, p.delta, (uint16_t*)p.dq, p.H, p.N, n_qtiles,
-                     (int)grid, c, p.scale);
+                     (const uint16_t*)p.dout, (const uint16_t*)p.o, p.lse, p.delta,
+                     (uint16_t*)p.dq, p.H, p.N, n_qtiles, (int)grid, c, p.scale);
 }
 
 // dQ summed with fp32 atomics across the KV-outer workgroups, then converted
@@ -710,17 +729,18 @@ hipError_t launch_bwd_atomic(const BwdParams& p) {
   return hipGetLastError();
 }
 
-// dQ from its own Q-outer pass (no atomics, no fp32 accumulator)
+// dQ from its own Q-outer pass (no atomics, no fp32 accumulator).  That pass
+// runs first and also computes D (the pre-processing step folded into it),
+// which the KV-outer dK/dV pass then reads.
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_two_pass(const BwdParams& p) {
   (void)hipGetLastError();
-  launch_preprocess<D, false>(p);
-  launch_kv_outer<D, CAUSAL, false>(p);
   constexpr int kCus = 256;
   const long long items8 =
       (long long)p.B * p.H * (CAUSAL ? ((p.N + 255) / 256 + 1) / 2 : (p.N + 255) / 256);
   if (items8 < 2 * kCus) launch_dq_pass<D, 4, CAUSAL>(p);
   else launch_dq_pass<D, 8, CAUSAL>(p);
+  launch_kv_outer<D, CAUSAL, false>(p);
   return hipGetLastError();
 }
 

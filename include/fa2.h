@@ -79,11 +79,11 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d, int causal);
 /*
  * Backward pass ("6.2 FlashAttention V2 in depth", section 7: P is recovered
  * from the saved logsumexp, dK and dV are owned by the block that holds a
- * key/value tile, and D_i = rowsum(dO_i * O_i) is computed once by a separate
- * pre-processing kernel).  dQ, which section 7.2 says must be summed across
- * the blocks of different key/value tiles, comes from a second pass over Q
- * tiles (the page's "two-pass" option): no atomics, and the result is
- * bitwise reproducible run to run.
+ * key/value tile, and D_i = rowsum(dO_i * O_i) is computed once per row
+ * rather than per tile).  dQ, which section 7.2 says must be summed across
+ * the blocks of different key/value tiles, comes from a separate pass over Q
+ * tiles (the page's "two-pass" option), which runs first and also computes
+ * D: no atomics, and the result is bitwise reproducible run to run.
  *   q, k, v : forward inputs, bf16 [B, N, H, d]
  *   o, lse  : forward outputs of fa2_fwd for the same q, k, v, causal, scale
  *   dout    : gradient of the loss w.r.t. o, bf16 [B, N, H, d]

@@ -140,11 +140,13 @@ def test_atomic_dq_backward_is_deterministic_in_dk_dv():
 
 
 def test_strategies_agree():
-    # the two dQ strategies sum the same products in different orders
+    # the two dQ strategies sum the same products in different orders (and
+    # compute D in different kernels), so they agree to rounding
     B, H, N, d = 1, 4, 520, 128
     x = make_inputs(B, H, N, d, seed=9, with_dout=True)
     a = run_bwd(x, True, d ** -0.5, False)
     b = run_bwd(x, True, d ** -0.5, True)
-    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
-    rel = (a[0].float() - b[0].float()).abs().max() / a[0].float().abs().max()
-    assert rel.item() <= 1e-2
+    assert torch.equal(a[2], b[2])  # dV does not depend on D
+    for ga, gb in zip(a, b):
+        rel = (ga.float() - gb.float()).abs().max() / ga.float().abs().max()
+        assert rel.item() <= 1e-2
