@@ -273,17 +273,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
                                      (void __attribute__((address_space(3)))*)(dst + m * 1024),
                                      16, 0, 0);
   };
+  // Q / dO DMA: this lane's row in the tile and swizzled element offset
+  int qd_row[NQI];
+  uint32_t qd_col[NQI];
+#pragma unroll
+  for (int u = 0; u < NQI; ++u) {
+    const unsigned ul = (unsigned)lane;
+    qd_row[u] = (wave * NQI + u) * RPI + (int)(ul / CPR);
+    qd_col[u] = (uint32_t)(((int)(ul % CPR) ^ SW::qd(qd_row[u])) * 8);
+  }
   auto issue_step = [&](int it, uint8_t* qd, uint8_t* dod, float* st)
       __attribute__((always_inline)) {
     const int q0 = it * kBwdQueries;
-    const int ln = (int)opaque((uint32_t)lane);
+    const int lim = N - 1 - q0;
+    const uint16_t* qb = q + head + (size_t)q0 * tok;
+    const uint16_t* db = dout + head + (size_t)q0 * tok;
 #pragma unroll
     for (int u = 0; u < NQI; ++u) {
-      dma_rows(q, q0, qd, wave * NQI + u, ln, [](int r) { return SW::qd(r); });
-      dma_rows(dout, q0, dod, wave * NQI + u, ln, [](int r) { return SW::qd(r); });
+      const int m = wave * NQI + u;
+      const uint32_t off = (uint32_t)(min(qd_row[u], lim) * (int)tok) + qd_col[u];
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(qb + off),
+                                       (void __attribute__((address_space(3)))*)(qd + m * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(db + off),
+                                       (void __attribute__((address_space(3)))*)(dod + m * 1024),
+                                       16, 0, 0);
     }
     if (wave < 2) {
-      const float* src = (wave == 0 ? lse : delta) + rowstat + q0 + min(ln, N - 1 - q0);
+      const float* src = (wave == 0 ? lse : delta) + rowstat + q0 + min(lane, lim);
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                        (void __attribute__((address_space(3)))*)(st + wave * kBwdQueries),
                                        4, 0, 0);
