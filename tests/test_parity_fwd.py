@@ -208,3 +208,27 @@ def test_split_kv_every_element(case, causal):
     o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal, d ** -0.5)
     rep = forward_report(o.cpu(), lse.cpu(), o_ref, lse_ref)
     assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("name,algo", [("fwd_b8_h16_n1024_d64_causal", "fa1-order"),
+                                       ("fwd_b1_h2_n16384_d128_full", "split-kv"),
+                                       ("fwd_b4_h16_n4096_d128_causal", "split-kv")])
+def test_other_forward_entry_points_full_size(name, algo):
+    # the ablation and split-KV entry points at full size, on sampled rows
+    w = WORKLOADS[name]
+    print(f"[fwd full-size {algo}] {w.name}", flush=True)
+    x = make_inputs(w.B, w.H, w.N, w.d, seed=w.seed, peaked_fraction=w.peaked_fraction)
+    d = _dev(x)
+    if algo == "fa1-order":
+        o, lse = binding.attention_forward_fa1_order(d["q"], d["k"], d["v"], w.causal, w.scale)
+    else:
+        o, lse = binding.attention_forward_split_kv(d["q"], d["k"], d["v"], w.causal, w.scale)
+    torch.cuda.synchronize()
+    del d
+    rows = sample_rows(w.B, w.H, w.N)
+    o_ref, lse_ref = oracle.attention_forward_rows(x["q"], x["k"], x["v"], w.causal, w.scale,
+                                                   rows)
+    b, h, i = (torch.as_tensor(rows[:, c], device="cuda") for c in range(3))
+    rep = forward_report(o[b, i, h].cpu(), lse[b, h, i].cpu(), o_ref, lse_ref)
+    print(f"  {rep}", flush=True)
+    assert rep["ok"], rep
