@@ -9,8 +9,9 @@
 //     both are built: a separate Q-outer dQ pass (launch_bwd, the default:
 //     deterministic and faster on MI355X) and fp32 atomics into a workspace
 //     accumulator (launch_bwd_atomic_dq).
-//   * D_i = rowsum(dO_i * O_i) is computed once by a separate pre-processing
-//     kernel (section 7.3) instead of tile by tile inside the main loop.
+//   * D_i = rowsum(dO_i * O_i) is computed once per row (section 7.3), not
+//     tile by tile: by the dQ pass, which runs first, on the two-pass path,
+//     and by a separate pre-processing kernel on the atomic path.
 // Gradient formulas (lost in the page's extraction; the standard softmax
 // gradient): dV = P^T dO, dP = dO V^T, dS = P * (dP - D), dK = scale dS^T Q,
 // dQ = scale dS K.
@@ -27,6 +28,9 @@
 //     LDS tiles; with the atomic dQ strategy, dS also goes to LDS, from which
 //     the workgroup forms its dQ partial = dS K over its 128 keys and adds it
 //     atomically.
+// For d = 128 the two-pass path runs bwd_kv_pair_kernel instead: the same
+// products with two waves per 32-key block, each taking half of every query
+// step, and V read from LDS, so that two waves fit per SIMD.
 #include <limits.h>
 #include <math.h>
 
@@ -701,6 +705,280 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
   }
 }
 
+// ----------------------------------------------------- B1, d = 128 ----
+// KV-outer dK/dV pass of the two-pass backward for d = 128, with two waves
+// per SIMD.  bwd_dl_kernel keeps K and V of its 32 keys in VGPRs and both
+// 32-query halves of a step in one wave: about 360 registers, so one wave per
+// SIMD and no other wave to run while it waits.  Here a workgroup has 8 waves
+// over the same 128 keys: wave w owns key block w % 4 and, of every 64-query
+// step, the half w / 4.  K rows stay in VGPRs (B operand of S); the V rows of
+// the 128 keys go to LDS once per work item and are read as the B operand of
+// dP (row reads, swizzled like the dQ pass's V tile).  That brings a wave
+// under 256 registers.  The two waves of a key block each hold a dK/dV partial
+// over their query halves; at the end one adds the other's through LDS and
+// writes the result, so each element is still written once and the pass stays
+// deterministic.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv_pair_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int H, int N, int n_ktiles, int grid, float c, float scale) {
+  constexpr int kWaves = 8;
+  constexpr int RB = D * 2;                  // bytes per row
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;             // rows per 1 KB DMA instruction
+  constexpr int QT = kBwdQueries * RB;       // bytes of a Q or dO tile
+  constexpr int VT = kBwdKeys * RB;          // bytes of the V tile
+  constexpr int NQI = QT / 1024 / kWaves;    // Q (and dO) DMA instructions per wave
+  constexpr int NVI = VT / 1024 / kWaves;    // V DMA instructions per wave
+  constexpr int DT = D / 32;
+  static_assert(NQI >= 1 && NVI >= 1, "tile split");
+  static_assert(16 * DT * 64 * 4 <= QT, "a wave's dK or dV partial fits one Q/dO buffer");
+  using SW = BwdSwz<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t v_s[VT];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_s0[QT];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_s1[QT];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_s0[QT];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_s1[QT];
+  __shared__ __attribute__((aligned(256))) float st_s0[2 * kBwdQueries];  // lse | delta
+  __shared__ __attribute__((aligned(256))) float st_s1[2 * kBwdQueries];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int l32 = lane % 32, hi = lane / 32;
+  const int kb = wave % 4;   // key block of the wave
+  const int qh = wave / 4;   // query half of every step
+
+  const int logical = xcd_contiguous_id(blockIdx.x, grid);
+  const int per_head = CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles;
+  const int bh = logical / per_head;
+  const int item = logical % per_head;
+  const int n_pass = (CAUSAL && item != n_ktiles - 1 - item) ? 2 : 1;
+  const int b = bh / H, hh = bh % H;
+  const size_t tok = (size_t)H * D;
+  const size_t head = (size_t)b * N * tok + (size_t)hh * D;
+  const size_t rowstat = ((size_t)b * H + hh) * N;
+
+  // Q / dO DMA: this lane's row in the tile and swizzled element offset
+  int qd_row[NQI];
+  uint32_t qd_col[NQI];
+#pragma unroll
+  for (int u = 0; u < NQI; ++u) {
+    const unsigned ul = (unsigned)lane;
+    qd_row[u] = (wave * NQI + u) * RPI + (int)(ul / CPR);
+    qd_col[u] = (uint32_t)(((int)(ul % CPR) ^ SW::qd(qd_row[u])) * 8);
+  }
+  auto issue_step = [&](int it, uint8_t* qd, uint8_t* dod, float* st)
+      __attribute__((always_inline)) {
+    const int q0 = it * kBwdQueries;
+    const int lim = N - 1 - q0;
+    const uint16_t* qb = q + head + (size_t)q0 * tok;
+    const uint16_t* db = dout + head + (size_t)q0 * tok;
+#pragma unroll
+    for (int u = 0; u < NQI; ++u) {
+      const int m = wave * NQI + u;
+      const uint32_t off = (uint32_t)(min(qd_row[u], lim) * (int)tok) + qd_col[u];
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(qb + off),
+                                       (void __attribute__((address_space(3)))*)(qd + m * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(db + off),
+                                       (void __attribute__((address_space(3)))*)(dod + m * 1024),
+                                       16, 0, 0);
+    }
+    if (wave < 2) {
+      const float* src = (wave == 0 ? lse : delta) + rowstat + q0 + min(lane, lim);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)(st + wave * kBwdQueries),
+                                       4, 0, 0);
+    }
+  };
+
+  // LDS read offsets, once per lane.  Q / dO rows: row t*32 + l%32, chunk
+  // 2*cc + hi at (row_base ^ (cc << 5)) + t * 32 * RB.  V rows (B operand of
+  // dP): key kb*32 + l%32, chunk 2*cc + hi at vrow_base ^ (cc << 5); the V
+  // swizzle depends on the row's low bits only.
+  uint32_t row_base = (uint32_t)(l32 * RB + ((hi ^ SW::qd(l32)) * 16));
+  uint32_t vrow_base = (uint32_t)(kb * 32 * RB + l32 * RB + ((hi ^ DqSwz<D>::v(l32)) * 16));
+  uint32_t trq[2];
+  tr_offsets<RB>(lane, [](int r) { return SW::qd(r); }, trq);
+
+  for (int pass = 0; pass < n_pass; ++pass) {
+    const int kt_idx = pass == 0 ? item : n_ktiles - 1 - item;
+    const int j0 = kt_idx * kBwdKeys;
+    const int kw0 = j0 + kb * 32;
+    const int my_key = kw0 + l32;
+
+    // V rows of the workgroup's 128 keys -> LDS (rows past N repeat row N-1)
+#pragma unroll
+    for (int u = 0; u < NVI; ++u) {
+      const int m = wave * NVI + u;
+      const int r = m * RPI + lane / CPR, slot = lane % CPR;
+      const uint32_t off =
+          (uint32_t)(min(r, N - 1 - j0) * (int)tok) + (uint32_t)((slot ^ DqSwz<D>::v(r)) * 8);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(v + head + (size_t)j0 * tok + off),
+          (void __attribute__((address_space(3)))*)(v_s + m * 1024), 16, 0, 0);
+    }
+    const int n_qtiles = (N + kBwdQueries - 1) / kBwdQueries;
+    const int it0 = CAUSAL ? j0 / kBwdQueries : 0;
+    if (it0 < n_qtiles) issue_step(it0, q_s0, do_s0, st_s0);
+
+    // K rows of this lane's key as B operands of S
+    bf16x8 kf[D / 16];
+    {
+      const size_t off = head + (size_t)min(my_key, N - 1) * tok + hi * 8;
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) {
+        u32x4 xk = *(const u32x4*)(k + off + cc * 16);
+        if (my_key >= N) xk = u32x4{0u, 0u, 0u, 0u};
+        kf[cc] = as_bf16x8(xk);
+      }
+    }
+
+    f32x16 dk_acc[DT], dv_acc[DT];
+    {
+      const bf16x8 z = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dk_acc[dt] = mfma32(z, z, f32x16{});
+        dv_acc[dt] = mfma32(z, z, f32x16{});
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+
+    auto step = [&](int it, const uint8_t* qs, const uint8_t* dos, const float* st, uint8_t* qn,
+                    uint8_t* don, float* stn) __attribute__((always_inline)) {
+      const int q0 = it * kBwdQueries;
+      if (it + 1 < n_qtiles) issue_step(it + 1, qn, don, stn);
+      row_base = opaque(row_base);
+      vrow_base = opaque(vrow_base);
+      trq[0] = opaque(trq[0]);
+      trq[1] = opaque(trq[1]);
+      const int qw = q0 + qh * 32;  // first query of this wave's half
+      {
+        const bool need_mask = (CAUSAL && kw0 + 31 > qw) || (qw + 32 > N) || (kw0 + 32 > N);
+        const int lo = CAUSAL ? my_key - q0 - 4 * hi : INT_MIN;
+        const int hi_lim = my_key < N ? N - q0 - 4 * hi : INT_MIN;
+        const int t = qh;
+        f32x16 s = f32x16{}, dp = f32x16{};
+        // Q, dO and V fragments two chunks ahead, fenced so the compiler
+        // neither hoists every read nor holds their registers
+        bf16x8 qa[2], da[2], va[2];
+        auto load = [&](int cc, int slot) __attribute__((always_inline)) {
+          const uint32_t off = (row_base ^ (uint32_t)(cc << 5)) + t * 32 * RB;
+          qa[slot] = *(const bf16x8*)(qs + off);
+          da[slot] = *(const bf16x8*)(dos + off);
+          va[slot] = *(const bf16x8*)(v_s + (vrow_base ^ (uint32_t)(cc << 5)));
+        };
+        load(0, 0);
+        load(1, 1);
+#pragma unroll
+        for (int cc = 0; cc < D / 16; ++cc) {
+          s = mfma32(qa[cc % 2], kf[cc], s);
+          dp = mfma32(da[cc % 2], va[cc % 2], dp);
+          if (cc + 2 < D / 16) load(cc + 2, cc % 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // P = exp2(S*c - L*log2e), dS = P * (dP - D); masked entries are 0
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qr = t * 32 + 8 * g + 4 * hi;
+          const f32x4 l4 = *(const f32x4*)(st + qr);
+          const f32x4 d4 = *(const f32x4*)(st + kBwdQueries + qr);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const int C = t * 32 + 8 * g + e;
+            float pr = fast_exp2(fmaf(s[r], c, -l4[e] * kLog2e));
+            if (need_mask && !(lo <= C && C < hi_lim)) pr = 0.f;
+            s[r] = pr;
+            dp[r] = pr * (dp[r] - d4[e]);
+          }
+        }
+
+        // dV += P^T dO and dK += dS^T Q over the wave's 32 queries; the
+        // transposed dO / Q fragments run one product pair ahead
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const int r0 = 8 * c2;
+          pf[c2] = to_bf16x8(f32x8{s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4], s[r0 + 5],
+                                   s[r0 + 6], s[r0 + 7]});
+          dsf[c2] = to_bf16x8(f32x8{dp[r0], dp[r0 + 1], dp[r0 + 2], dp[r0 + 3], dp[r0 + 4],
+                                    dp[r0 + 5], dp[r0 + 6], dp[r0 + 7]});
+        }
+        constexpr int kPairs = 2 * DT;  // (c2, dt) pairs
+        bf16x8 ofr[2], qfr[2];
+        auto tload = [&](int i, int slot) __attribute__((always_inline)) {
+          const int c2 = i / DT, dt = i % DT;
+          ofr[slot] = tr_frag<RB>(dos, trq, dt, 2 * t + c2);
+          qfr[slot] = tr_frag<RB>(qs, trq, dt, 2 * t + c2);
+        };
+        tload(0, 0);
+        tload(1, 1);
+#pragma unroll
+        for (int i = 0; i < kPairs; ++i) {
+          const int c2 = i / DT, dt = i % DT;
+          dv_acc[dt] = mfma32(pf[c2], ofr[i % 2], dv_acc[dt]);
+          dk_acc[dt] = mfma32(dsf[c2], qfr[i % 2], dk_acc[dt]);
+          if (i + 2 < kPairs) tload(i + 2, i % 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // next step's tiles have landed
+      __syncthreads();
+    };
+    for (int it = it0; it < n_qtiles; it += 2) {
+      step(it, q_s0, do_s0, st_s0, q_s1, do_s1, st_s1);
+      if (it + 1 < n_qtiles) step(it + 1, q_s1, do_s1, st_s1, q_s0, do_s0, st_s0);
+    }
+
+    // The two waves of a key block add their partials through LDS (the Q/dO
+    // buffers are free now): the upper half stores, the lower half adds and
+    // writes out.  Layout [register][lane] keeps the accesses conflict-free.
+    uint8_t* const red = kb == 0 ? q_s0 : kb == 1 ? q_s1 : kb == 2 ? do_s0 : do_s1;
+    auto put = [&](const f32x16* acc) __attribute__((always_inline)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ((float*)red)[(dt * 16 + r) * 64 + lane] = acc[dt][r];
+    };
+    auto add_store = [&](const f32x16* acc, uint16_t* dst, float mul) __attribute__((always_inline)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = acc[dt][r] + ((const float*)red)[(dt * 16 + r) * 64 + lane];
+          const int key = kw0 + acc_row(r, hi);
+          if (key < N) dst[head + (size_t)key * tok + dt * 32 + l32] = to_bf16_bits(mul * x);
+        }
+    };
+    if (qh == 1) put(dk_acc);
+    __syncthreads();
+    if (qh == 0) add_store(dk_acc, dk, scale);
+    __syncthreads();
+    if (qh == 1) put(dv_acc);
+    __syncthreads();
+    if (qh == 0) add_store(dv_acc, dv, 1.0f);
+    __syncthreads();
+  }
+}
+
+template <int D, bool CAUSAL>
+void launch_kv_pair(const BwdParams& p) {
+  const int n_ktiles = (p.N + kBwdKeys - 1) / kBwdKeys;
+  const long long grid = (long long)p.B * p.H * (CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles);
+  const float c = (float)((double)p.scale * 1.4426950408889634);
+  hipLaunchKernelGGL((bwd_kv_pair_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(512), 0, p.stream,
+                     (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
+                     (const uint16_t*)p.dout, p.lse, p.delta, (uint16_t*)p.dk, (uint16_t*)p.dv,
+                     p.H, p.N, n_ktiles, (int)grid, c, p.scale);
+}
+
+
 // B0 launch: D (and, for the atomic dQ sum, the zeroed accumulator)
 template <int D, bool ZERO_DQ>
 void launch_preprocess(const BwdParams& p) {
@@ -757,7 +1035,10 @@ hipError_t launch_bwd_two_pass(const BwdParams& p) {
       (long long)p.B * p.H * (CAUSAL ? ((p.N + 255) / 256 + 1) / 2 : (p.N + 255) / 256);
   if (items8 < 2 * kCus) launch_dq_pass<D, 4, CAUSAL>(p);
   else launch_dq_pass<D, 8, CAUSAL>(p);
-  launch_kv_outer<D, CAUSAL, false>(p);
+  // d = 128: the 8-wave pass (two waves per SIMD); d = 64 fits two 4-wave
+  // workgroups per CU already, where the 4-wave pass measures faster
+  if constexpr (D == 128) launch_kv_pair<D, CAUSAL>(p);
+  else launch_kv_outer<D, CAUSAL, false>(p);
   return hipGetLastError();
 }
 

@@ -139,14 +139,17 @@ def test_atomic_dq_backward_is_deterministic_in_dk_dv():
     assert np.isfinite(r1[0].float().cpu().numpy()).all()
 
 
-def test_strategies_agree():
+@pytest.mark.parametrize("d", [64, 128])
+def test_strategies_agree(d):
     # the two dQ strategies sum the same products in different orders (and
     # compute D in different kernels), so they agree to rounding
-    B, H, N, d = 1, 4, 520, 128
+    B, H, N = 1, 4, 520
     x = make_inputs(B, H, N, d, seed=9, with_dout=True)
     a = run_bwd(x, True, d ** -0.5, False)
     b = run_bwd(x, True, d ** -0.5, True)
-    assert torch.equal(a[2], b[2])  # dV does not depend on D
+    if d == 64:
+        # same KV-outer kernel on both paths, and dV does not depend on D
+        assert torch.equal(a[2], b[2])
     for ga, gb in zip(a, b):
         rel = (ga.float() - gb.float()).abs().max() / ga.float().abs().max()
         assert rel.item() <= 1e-2
