@@ -357,6 +357,277 @@ hipError_t launch_fwd_dl(const FwdParams& p) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined variant for non-causal d = 128.  Per wave and K/V tile
+// the loop body is the same arithmetic as fwd_dl_kernel's, reordered so the
+// matrix cores and the vector ALUs work on different tiles: iteration j
+// issues the MFMAs of S(j+1) = K(j+1) Q^T while the VALU forms
+// P(j) = exp2(S(j) c - m), then the MFMAs of O += V(j)^T P(j)^T while the VALU
+// takes the max of S(j+1).  K therefore runs one tile ahead of V: at step j the
+// DMA fills K(j+2) into the buffer K(j) used and V(j+1) into the one V(j-1)
+// used.  Tiles that need the element mask (the ragged end) take the plain
+// one-tile-per-step path after the pipelined loop.
+template <int D, int BC, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W))) void fwd_sp_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
+    int H, int N, int n_qtiles, int grid, float c, uint32_t q_and, uint32_t q_xor) {
+  constexpr int BR = W * 32;
+  constexpr int RB = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 1024 / RB;
+  constexpr int TILE = BC * RB;
+  constexpr int NI = TILE / 1024;
+  constexpr int NIW = NI / W;
+  static_assert(NI % W == 0 && NIW >= 1, "tile must split evenly over the waves");
+  using SW = DlSwz<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1[TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int l32 = lane % 32, hi = lane / 32;
+
+  const int logical = xcd_contiguous_id(blockIdx.x, grid);
+  const int bh = logical / n_qtiles;
+  const int qt = logical % n_qtiles;
+  const int b = bh / H, hh = bh % H;
+  const size_t tok = (size_t)H * D;
+  const size_t head = (size_t)b * N * tok + (size_t)hh * D;
+  const int qw0 = qt * BR + wave * 32;
+  const int my_q = qw0 + l32;
+
+  uint32_t koff[NIW], voff[NIW];
+  int lrow[NIW];
+#pragma unroll
+  for (int u = 0; u < NIW; ++u) {
+    const int m = wave * NIW + u;
+    const int r = m * RPI + lane / CPR, slot = lane % CPR;
+    lrow[u] = r;
+    koff[u] = (uint32_t)(r * tok * 2) + (uint32_t)((slot ^ SW::k(r)) * 16);
+    voff[u] = (uint32_t)(r * tok * 2) + (uint32_t)((slot ^ SW::v(r)) * 16);
+  }
+  // DMA of one tensor's tile jt into dst (rows past N repeat row N-1)
+  auto issue_one = [&](const uint16_t* src, const uint32_t* off, int jt, uint8_t* dst)
+      __attribute__((always_inline)) {
+    const int kv0 = jt * BC;
+    const uint8_t* base = (const uint8_t*)(src + head + (size_t)kv0 * tok);
+    const bool whole = kv0 + BC <= N;
+#pragma unroll
+    for (int u = 0; u < NIW; ++u) {
+      const int m = wave * NIW + u;
+      uint32_t x = off[u];
+      if (!whole) x -= (uint32_t)(max(kv0 + lrow[u] - (N - 1), 0) * tok * 2);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(base + x),
+                                       (void __attribute__((address_space(3)))*)(dst + m * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  const int n_kv = (N + BC - 1) / BC;
+  const int n_main = N / BC;  // tiles with no masked key
+  issue_one(k, koff, 0, kb0);
+  issue_one(v, voff, 0, vb0);
+  if (n_kv > 1) issue_one(k, koff, 1, kb1);
+
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qp = q + head + (size_t)min(my_q, N - 1) * tok + 8 * hi;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      u32x4 x = *(const u32x4*)(qp + 16 * cc);
+      if (my_q >= N) x = u32x4{0u, 0u, 0u, 0u};
+      x = (x & q_and) ^ q_xor;
+      qf[cc] = as_bf16x8(x);
+    }
+  }
+
+  // S^T = K Q^T for the tile in kb; row kt*32 + l32's swizzle depends on l32
+  // only, so chunk cc*2+hi sits at kbase ^ (cc << 5) in every kt block
+  const uint32_t kbase = (uint32_t)(l32 * RB) + (uint32_t)((hi ^ SW::k(l32)) * 16);
+  auto scores = [&](const uint8_t* kb, f32x16* s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      const uint32_t off = kbase ^ (uint32_t)(cc << 5);
+#pragma unroll
+      for (int kt = 0; kt < BC / 32; ++kt) {
+        const bf16x8 a = *(const bf16x8*)(kb + kt * 32 * RB + off);
+        s[kt] = mfma32(a, qf[cc], cc == 0 ? f32x16{} : s[kt]);
+      }
+    }
+  };
+  // tile max in log2 units (-inf for a row with no visible key)
+  auto tile_max = [&](const f32x16* s) __attribute__((always_inline)) {
+    float mx = max2f(s[0][0], s[0][1]);
+#pragma unroll
+    for (int i = 2; i < BC / 2; i += 2) mx = max3f(mx, s[i / 16][i % 16], s[i / 16][i % 16 + 1]);
+    mx = pair_max(mx);
+    return (mx == -INFINITY) ? -INFINITY : mx * c;
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+  // lazy rescale (see fwd_dl_kernel); returns the reference the tile's P uses
+  auto rescale_to = [&](float mt) __attribute__((always_inline)) {
+    if (wave_any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
+    return (m_run == -INFINITY) ? 0.f : m_run;
+  };
+  // P = exp2(S c - mref) in bf16, and its fp32 row sum
+  auto probs = [&](const f32x16* sc, float mref, bf16x8* pf) __attribute__((always_inline)) {
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < BC / 16; ++cc) {
+      f32x8 p8;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        p8[t] = fast_exp2(fmaf(sc[cc / 2][8 * (cc % 2) + t], c, -mref));
+        if (t % 2) rs1 += p8[t];
+        else rs0 += p8[t];
+      }
+      pf[cc] = to_bf16x8(p8);
+    }
+    return rs0 + rs1;
+  };
+  // O^T += V^T P^T; the V^T fragment of row 16cc + 8u + 4hi + i4, columns
+  // dt*32 + 16(g16%2) + 4a4 .. +3 sits at vbase ^ (dt << 6) + (16cc + 8u) RB
+  const int g16 = lane / 16, i4 = (lane % 16) / 4, a4 = lane % 4;
+  const uint32_t vbase = (uint32_t)((4 * hi + i4) * RB) +
+                         (uint32_t)(((2 * (g16 % 2) + a4 / 2) ^ SW::v(4 * hi + i4)) * 16) +
+                         (uint32_t)((4 * a4) % 8 * 2);
+  auto pv = [&](const uint8_t* vb, const bf16x8* pf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < BC / 16; ++cc)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const uint32_t off = vbase ^ (uint32_t)(dt << 6);
+        u32x2 part[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          part[u] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (short __attribute__((ext_vector_type(4))) __attribute__((address_space(3)))*)(
+                             vb + (16 * cc + 8 * u) * RB + off)));
+        oacc[dt] = mfma32(as_bf16x8(u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}), pf[cc],
+                          oacc[dt]);
+      }
+  };
+
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // K(0), V(0), K(1) and Q have landed
+  __syncthreads();
+  f32x16 sa[BC / 32], sb[BC / 32];
+  float mt = -INFINITY;
+  if (n_main > 0) {
+    scores(kb0, sa);
+    mt = tile_max(sa);
+  }
+  __syncthreads();  // every wave has read K(0): kb0 may take K(2)
+
+  // pipelined step jt < n_main - 1: S(jt+1) and P(jt), then O += V(jt) P(jt)
+  // and the max of S(jt+1)
+  auto full = [&](int jt, const f32x16* sc, f32x16* sn, const uint8_t* k_next, const uint8_t* v_cur,
+                  uint8_t* k_dma, uint8_t* v_dma) __attribute__((always_inline)) {
+    if (jt + 2 < n_kv) issue_one(k, koff, jt + 2, k_dma);
+    issue_one(v, voff, jt + 1, v_dma);
+    const float mref = rescale_to(mt);
+    bf16x8 pf[BC / 16];
+    scores(k_next, sn);
+    const float rs = probs(sc, mref, pf);
+    pv(v_cur, pf);
+    mt = tile_max(sn);
+    l_part += rs;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+  // last unmasked tile: P and O only; starts the loads the ragged tile needs
+  auto drain = [&](int jt, const f32x16* sc, const uint8_t* v_cur, uint8_t* k_dma, uint8_t* v_dma)
+      __attribute__((always_inline)) {
+    if (jt + 2 < n_kv) issue_one(k, koff, jt + 2, k_dma);
+    if (jt + 1 < n_kv) issue_one(v, voff, jt + 1, v_dma);
+    const float mref = rescale_to(mt);
+    bf16x8 pf[BC / 16];
+    const float rs = probs(sc, mref, pf);
+    pv(v_cur, pf);
+    l_part += rs;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+  int jt = 0;
+  for (; jt + 2 < n_main; jt += 2) {
+    full(jt, sa, sb, kb1, vb0, kb0, vb1);
+    full(jt + 1, sb, sa, kb0, vb1, kb1, vb0);
+  }
+  if (jt + 1 < n_main) {
+    full(jt, sa, sb, kb1, vb0, kb0, vb1);
+    drain(jt + 1, sb, vb1, kb1, vb0);
+    jt += 2;
+  } else if (jt < n_main) {
+    drain(jt, sa, vb0, kb0, vb1);
+    jt += 1;
+  }
+  // the ragged last tile (keys past N masked); K(jt), V(jt) are in buffer jt % 2
+  if (jt < n_kv) {
+    const uint8_t* kc = (jt % 2) ? kb1 : kb0;
+    const uint8_t* vc = (jt % 2) ? vb1 : vb0;
+    f32x16 st[BC / 32];
+    scores(kc, st);
+    const int kv0 = jt * BC;
+#pragma unroll
+    for (int kt = 0; kt < BC / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kv0 + kt * 32 + acc_row(r, hi) >= N) st[kt][r] = -INFINITY;
+    const float mref = rescale_to(tile_max(st));
+    bf16x8 pf[BC / 16];
+    const float rs = probs(st, mref, pf);
+    pv(vc, pf);
+    l_part += rs;
+  }
+
+  const float l = pair_sum(l_part);
+  const float inv = 1.0f / l;
+  if (my_q < N) {
+    uint16_t* op = o + head + (size_t)my_q * tok;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = f32x4{oacc[dt][4 * g + 0], oacc[dt][4 * g + 1], oacc[dt][4 * g + 2],
+                              oacc[dt][4 * g + 3]} * inv;
+        *(u32x2*)(op + dt * 32 + 8 * g + 4 * hi) = __builtin_bit_cast(u32x2, to_bf16x4(x));
+      }
+    if (hi == 0) lse[((size_t)b * H + hh) * N + my_q] = (m_run + log2f(l)) * kLn2;
+  }
+}
+
+template <int D, int BC, int W>
+hipError_t launch_fwd_sp(const FwdParams& p) {
+  constexpr int BR = W * 32;
+  const int n_qtiles = (p.N + BR - 1) / BR;
+  const long long grid = (long long)p.B * p.H * n_qtiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
+  const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
+  const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((fwd_sp_kernel<D, BC, W>), dim3((unsigned)grid), dim3(W * 64), 0, p.stream,
+                     (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
+                     (uint16_t*)p.o, p.lse, p.H, p.N, n_qtiles, (int)grid, c, q_and, q_xor);
+  return hipGetLastError();
+}
+
 // Split-KV merge: for every row, L = log2 sum_s 2^{L_s} and
 // O = sum_s 2^{L_s - L} O_s, i.e. the slices' softmax sums re-weighted to the
 // whole key range (each O_s was normalised by its own sum).  One thread per
@@ -422,7 +693,9 @@ hipError_t launch_fwd(const FwdParams& p) {
   // grids of fewer than two 8-wave workgroups per CU use the 4-wave tiles.
   constexpr int kCus = 256;
   if (!p.causal) {
-    return p.d == 64 ? launch_fwd_dl<64, 64, 8, 2, false>(p) : launch_fwd_dl<128, 64, 8, 2, false>(p);
+    // d = 128: the software-pipelined kernel (the VALU work of one tile under
+    // the MFMAs of the next); at d = 64 the plain kernel measures faster
+    return p.d == 64 ? launch_fwd_dl<64, 64, 8, 2, false>(p) : launch_fwd_sp<128, 64, 8>(p);
   }
   const long long pairs8 = (long long)p.B * p.H * (((p.N + 255) / 256 + 1) / 2);
   const bool small = pairs8 < 2 * kCus;
