@@ -59,6 +59,9 @@ SMALL = [
     (1, 2, 257, 128),
     (2, 1, 64, 128),
     (1, 1, 700, 64),
+    (1, 1, 1, 128),      # a single token
+    (1, 1, 130, 128),    # two key tiles, the second two keys long
+    (2, 2, 600, 128),    # odd key-tile count: the middle causal tile runs alone
 ]
 
 
@@ -76,10 +79,11 @@ def test_small_shapes_every_element(shape, causal, atomic_dq):
     check(grads, ref, heads, f"{shape} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale", [-0.1, 0.3])
-def test_unusual_scales(scale):
-    B, H, N, d = 1, 2, 190, 64
-    print(f"[bwd scale] scale={scale}", flush=True)
+def test_unusual_scales(scale, d):
+    B, H, N = 1, 2, 190
+    print(f"[bwd scale] scale={scale} d={d}", flush=True)
     x = make_inputs(B, H, N, d, seed=4, with_dout=True)
     grads = run_bwd(x, True, scale)
     heads = [(0, 0), (0, 1)]

@@ -41,6 +41,14 @@ SMALL_SHAPES = [
     (1, 1, 1000, 64),
     (3, 2, 129, 64),
     (1, 1, 520, 128),
+    # d = 128 non-causal runs the pipelined kernel: cover each way its loop
+    # can end (drain after one or two full steps, with and without the
+    # ragged tile, in either buffer)
+    (1, 1, 128, 128),
+    (1, 2, 100, 128),
+    (2, 1, 200, 128),
+    (1, 1, 192, 128),
+    (1, 1, 63, 128),
 ]
 
 
@@ -57,12 +65,13 @@ def test_small_shapes_every_element(shape, causal):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1.0 / 128])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_unusual_scales(scale, causal):
-    B, H, N, d = 1, 2, 300, 64
+def test_unusual_scales(scale, causal, d):
+    B, H, N = 1, 2, 300
     x = make_inputs(B, H, N, d, seed=5, peaked_fraction=0.02)
-    print(f"[fwd scale] scale={scale} causal={causal}", flush=True)
+    print(f"[fwd scale] scale={scale} causal={causal} d={d}", flush=True)
     o, lse = run_fwd(x, causal, scale)
     o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal, scale)
     rep = forward_report(o, lse, o_ref, lse_ref)
