@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
   for (int u = 0; u < NKI; ++u)
     if constexpr (ATOMIC_DQ) dma_rows(k, j0, kt_s, wave * NKI + u, lane, [](int r) { return SW::k(r); });
   if (it0 < n_qtiles) issue_step(it0, q_s0, do_s0, st_s0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  wait_dma_and_lds();  // the first tiles have landed
   __syncthreads();
 
   constexpr int kTilesPerWave = D / 64;  // 32x32 dQ tiles per wave per step
@@ -436,6 +436,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
     }
 
     if constexpr (ATOMIC_DQ) {
+    wait_dma_and_lds();
     __syncthreads();
 
     // dQ partial = scale * dS K over this workgroup's 128 keys.  Its atomic
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
     }
     q0_pend = q0;
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // next step's tiles have landed
+    wait_dma_and_lds();  // next step's tiles have landed
     __syncthreads();
   };
   for (int it = it0; it < n_qtiles; it += 2) {
@@ -677,13 +678,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
     };
 
     if (n_kv > 0) issue(0, kb0, vb0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 has landed
+    wait_dma_and_lds();  // tile 0 has landed
     __syncthreads();
     auto step = [&](int jt, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn)
         __attribute__((always_inline)) {
       issue(min(jt + 1, n_kv - 1), kn, vn);
       if (!CAUSAL || jt * BC <= qw0 + 31) tile(jt, kc, vc);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile jt+1 has landed
+      wait_dma_and_lds();  // tile jt+1 has landed
       __syncthreads();
     };
     for (int jt = 0; jt < n_kv; jt += 2) {
@@ -845,7 +846,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         dv_acc[dt] = mfma32(z, z, f32x16{});
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    wait_dma_and_lds();  // the first tiles have landed
     __syncthreads();
 
     auto step = [&](int it, const uint8_t* qs, const uint8_t* dos, const float* st, uint8_t* qn,
@@ -928,7 +929,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // next step's tiles have landed
+      wait_dma_and_lds();  // next step's tiles have landed
       __syncthreads();
     };
     for (int it = it0; it < n_qtiles; it += 2) {
@@ -957,12 +958,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         }
     };
     if (qh == 1) put(dk_acc);
+    wait_dma_and_lds();
     __syncthreads();
     if (qh == 0) add_store(dk_acc, dk, scale);
+    wait_dma_and_lds();
     __syncthreads();
     if (qh == 1) put(dv_acc);
+    wait_dma_and_lds();
     __syncthreads();
     if (qh == 0) add_store(dv_acc, dv, 1.0f);
+    wait_dma_and_lds();
     __syncthreads();
   }
 }

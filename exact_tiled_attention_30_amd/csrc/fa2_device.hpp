@@ -60,18 +60,19 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, kWave);
 }
 
-// v_max3_f32 / v_max_f32 without the NaN-quieting canonicalisation the
-// compiler wraps around fmaxf in IEEE mode (scores are finite or -inf; a NaN
-// input still propagates through the exp).
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float max2f(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
+// Max of a lane's scores, written with fmaxf so the compiler forms the
+// v_max3_f32 chain itself.  It must stay compiler-visible: the hazard
+// recognizer pads a VALU read of an MFMA result only when it can see the
+// instruction, and a hand-written v_max reading an accumulator right after
+// its MFMA was observed to see a partial sum (a race that only moved the
+// lazy-rescale reference, so results differed from run to run by rounding).
+// NaN handling is IEEE (the compiler canonicalises the first pair).
+template <int NV>
+__device__ __forceinline__ float lane_max(const f32x16* s) {
+  float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int i = 2; i < NV; i += 2) mx = fmaxf(fmaxf(mx, s[i / 16][i % 16]), s[i / 16][i % 16 + 1]);
+  return mx;
 }
 
 // max / sum of a value over the lane pair (l, l ^ 32) with one
@@ -81,7 +82,7 @@ __device__ __forceinline__ float max2f(float a, float b) {
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return max2f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -94,6 +95,16 @@ __device__ __forceinline__ bool wave_any(bool p) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt in
+// bits 6:4, lgkmcnt in bits 11:8).  Before a barrier after which another
+// wave's global_load_lds may overwrite an LDS buffer, a wave must have both
+// its own DMA landed (vmcnt) and its own LDS reads of that buffer returned
+// (lgkmcnt): the workgroup fence of __syncthreads() orders LDS accesses
+// among waves but not a read still in flight against a DMA write, and the
+// compiler may schedule a read's consumer after the barrier.
+constexpr int kWaitVmLgkm = 0x0070;  // vmcnt(0) lgkmcnt(0)
+__device__ __forceinline__ void wait_dma_and_lds() { __builtin_amdgcn_s_waitcnt(kWaitVmLgkm); }
 
 // Workgroups are dispatched round-robin over the eight XCDs (wg i runs on XCD
 // i % 8).  Renumber them so that each XCD receives one contiguous range of

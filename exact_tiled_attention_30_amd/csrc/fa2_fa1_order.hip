@@ -64,6 +64,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void f
   for (int jt = 0; jt < n_kv; ++jt) {
     const int kv0 = jt * BC;
     // load K_j, V_j (every wave is done with the previous tile)
+    wait_dma_and_lds();
     __syncthreads();
     {
       const uint8_t* kbase = (const uint8_t*)(k + head + (size_t)kv0 * tok);
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void f
             (void __attribute__((address_space(3)))*)(vb + m * 1024), 16, 0, 0);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    wait_dma_and_lds();  // the first tiles have landed
     __syncthreads();
 
     const int it0 = CAUSAL ? kv0 / BR : 0;  // first Q tile that sees this K/V tile
@@ -147,9 +148,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void f
             if (!(key < N && (!CAUSAL || key <= my_q))) s[kt][r] = -INFINITY;
           }
       }
-      float mx = max2f(s[0][0], s[0][1]);
-#pragma unroll
-      for (int i = 2; i < BC / 2; i += 2) mx = max3f(mx, s[i / 16][i % 16], s[i / 16][i % 16 + 1]);
+      float mx = lane_max<BC / 2>(s);
       mx = pair_max(mx);
       const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
       const float m_new = fmaxf(m_old, mt);

@@ -221,9 +221,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
           if (!visible) s[kt][r] = -INFINITY;
         }
     }
-    float mx = max2f(s[0][0], s[0][1]);
-#pragma unroll
-    for (int i = 2; i < BC / 2; i += 2) mx = max3f(mx, s[i / 16][i % 16], s[i / 16][i % 16 + 1]);
+    float mx = lane_max<BC / 2>(s);
     mx = pair_max(mx);
     const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
     if (wave_any(mt > m_run + kRescaleSlack)) {
@@ -276,7 +274,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   // clamped at the end), so the wait before each barrier is "all but the
   // newest STAGES-2 batches" -- which leaves tile jt+1 landed.
   static_assert(2 * NIW * (STAGES - 1) <= 15, "vmcnt immediate");
-  constexpr int kWaitStep = 0x0F70 | (2 * NIW * (STAGES - 2));
+  constexpr int kWaitStep = kWaitVmLgkm | (2 * NIW * (STAGES - 2));  // lgkmcnt(0) too
   __builtin_amdgcn_s_waitcnt(kWaitStep);  // tile 0 (and Q) have landed
   __syncthreads();
 
@@ -299,7 +297,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
       if (jt + 1 < n_kv) step(jt + 1, kb1, vb1, kb0, vb0);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // drain the LDS DMA before exit
+  wait_dma_and_lds();  // drain the LDS DMA before exit
 
   const float l = pair_sum(l_part);
   if constexpr (SPLIT) {
@@ -336,7 +334,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
     if (hi == 0) lse[((size_t)b * H + hh) * N + my_q] = (m_run + log2f(l)) * kLn2;
   }
   }
-  if (pass + 1 < n_pass) __syncthreads();  // every wave is done with the LDS tiles
+  if (pass + 1 < n_pass) {
+    wait_dma_and_lds();
+    __syncthreads();  // every wave is done with the LDS tiles
+  }
   }
 }
 
@@ -460,9 +461,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
   };
   // tile max in log2 units (-inf for a row with no visible key)
   auto tile_max = [&](const f32x16* s) __attribute__((always_inline)) {
-    float mx = max2f(s[0][0], s[0][1]);
-#pragma unroll
-    for (int i = 2; i < BC / 2; i += 2) mx = max3f(mx, s[i / 16][i % 16], s[i / 16][i % 16 + 1]);
+    float mx = lane_max<BC / 2>(s);
     mx = pair_max(mx);
     return (mx == -INFINITY) ? -INFINITY : mx * c;
   };
@@ -524,7 +523,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
       }
   };
 
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // K(0), V(0), K(1) and Q have landed
+  wait_dma_and_lds();  // K(0), V(0), K(1) and Q have landed
   __syncthreads();
   f32x16 sa[BC / 32], sb[BC / 32];
   float mt = -INFINITY;
@@ -532,6 +531,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
     scores(kb0, sa);
     mt = tile_max(sa);
   }
+  wait_dma_and_lds();
   __syncthreads();  // every wave has read K(0): kb0 may take K(2)
 
   // pipelined step jt < n_main - 1: S(jt+1) and P(jt), then O += V(jt) P(jt)
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
     pv(v_cur, pf);
     mt = tile_max(sn);
     l_part += rs;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    wait_dma_and_lds();
     __syncthreads();
   };
   // last unmasked tile: P and O only; starts the loads the ragged tile needs
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
     const float rs = probs(sc, mref, pf);
     pv(v_cur, pf);
     l_part += rs;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    wait_dma_and_lds();
     __syncthreads();
   };
   int jt = 0;
