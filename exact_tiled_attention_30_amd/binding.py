@@ -64,6 +64,8 @@ def lib():
     L.fa2_fwd_fa1_order.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i, _i, _i, _i,
                                     _i, ctypes.c_float, _vp]
     L.fa2_fwd_fa1_order.restype = _i
+    L.fa2_calibrate_mfma.argtypes = [_vp, _i, _i, _vp]
+    L.fa2_calibrate_mfma.restype = _i
     L.fa2_status_string.argtypes = [_i]
     L.fa2_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -72,6 +74,18 @@ def lib():
 
 def fa2_status_string(status: int) -> str:
     return lib().fa2_status_string(int(status)).decode()
+
+
+def fa2_calibrate_mfma(out, blocks: int, iters: int, stream=None) -> None:
+    """Measurement helper: `blocks` x 256 threads of back-to-back bf16 MFMAs
+    (blocks x 4 x iters x 4 x 32768 FLOP); `out` a float32 device tensor of
+    at least blocks x 256 elements.  Time it with events on `stream`."""
+    import torch
+
+    _require(out, torch.float32, "out")
+    if out.numel() < blocks * 256:
+        raise ValueError("out is too small")
+    _check(lib().fa2_calibrate_mfma(_ptr(out), int(blocks), int(iters), _stream(out, stream)))
 
 
 def _check(status: int) -> None:

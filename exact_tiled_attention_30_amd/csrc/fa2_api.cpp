@@ -241,6 +241,14 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
                     causal, scale, stream, false);
 }
 
+int fa2_calibrate_mfma(float* out, int blocks, int iters, void* stream) {
+  if (out == nullptr) return FA2_ERR_NULLPTR;
+  if (blocks < 1 || iters < 1) return FA2_ERR_SHAPE;
+  return fa2::launch_calib_mfma(out, blocks, iters, (hipStream_t)stream) == hipSuccess
+             ? FA2_OK
+             : FA2_ERR_LAUNCH;
+}
+
 int fa2_bwd_atomic_dq(const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,

@@ -171,6 +171,19 @@ int fa2_fwd_fa1_order(const void* q, const void* k, const void* v, void* o, floa
                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                       int causal, float scale, void* stream);
 
+/* Measurement helper, not part of the attention path: runs `blocks`
+ * workgroups of 256 threads in which every wave issues iters x 4
+ * v_mfma_f32_32x32x16_bf16 (32768 FLOP each) from registers, so the caller
+ * can time it and read the bf16 MFMA throughput at the GPU's running clock,
+ * the yardstick for the nominal dense peak (MI355X data sheet: 256 CUs x
+ * 4096 FLOP/clk x 2.4 GHz).  FLOPs per call = blocks x 4 x iters x 4 x 32768.
+ * out: device buffer of at least blocks x 256 floats (caller-owned; the
+ * values are meaningless, they keep the work alive).  Errors: FA2_ERR_NULLPTR
+ * if out is NULL, FA2_ERR_SHAPE if blocks < 1 or iters < 1, FA2_ERR_LAUNCH.
+ * Asynchronous on `stream`.
+ */
+int fa2_calibrate_mfma(float* out, int blocks, int iters, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa2_status_string(int status);
 

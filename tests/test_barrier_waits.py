@@ -64,5 +64,6 @@ def unguarded_barriers(lines):
 def test_every_barrier_waits_for_lds_and_dma(src):
     with tempfile.TemporaryDirectory() as d:
         lines = _asm(src, d)
-    assert any("s_barrier" in l for l in lines)
+    if src != "fa2_calib.hip":  # the MFMA yardstick has no LDS and no barrier
+        assert any("s_barrier" in l for l in lines)
     assert unguarded_barriers(lines) == []
