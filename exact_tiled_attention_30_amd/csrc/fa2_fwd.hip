@@ -69,7 +69,10 @@ struct DlSwz {
 // SPLIT: the key range of every Q tile is cut into n_split slices, one work
 // item each; a slice's normalised O (fp32) and its logsumexp (log2 units) go
 // to o_part / lse_part, and fwd_combine_kernel merges them.
-template <int D, int BC, int W, int STAGES, bool CAUSAL, bool SPLIT = false>
+// PAIR (causal): a work item is a heavy + light pair of Q tiles; without it,
+// one Q tile, heaviest first -- for grids too small to fill the GPU, where
+// twice the workgroups beat the balance.
+template <int D, int BC, int W, int STAGES, bool CAUSAL, bool SPLIT = false, bool PAIR = true>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 1))) void fwd_dl_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -103,10 +106,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   const int logical0 = xcd_contiguous_id(blockIdx.x, grid);
   const int split = SPLIT ? logical0 % n_split : 0;  // slices of one Q tile are adjacent
   const int logical = SPLIT ? logical0 / n_split : logical0;
-  const int per_head = (CAUSAL && !SPLIT) ? (n_qtiles + 1) / 2 : n_qtiles;
+  const int per_head = (CAUSAL && !SPLIT && PAIR) ? (n_qtiles + 1) / 2 : n_qtiles;
   const int bh = logical / per_head;
   const int item = logical % per_head;
-  const int n_pass = (CAUSAL && !SPLIT && item != n_qtiles - 1 - item) ? 2 : 1;
+  const int n_pass = (CAUSAL && !SPLIT && PAIR && item != n_qtiles - 1 - item) ? 2 : 1;
   const int b = bh / H, hh = bh % H;
   const size_t tok = (size_t)H * D;
   const size_t head = (size_t)b * N * tok + (size_t)hh * D;
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   };
 
   for (int pass = 0; pass < n_pass; ++pass) {
-  const int qt = (CAUSAL && !SPLIT) ? (pass == 0 ? n_qtiles - 1 - item : item) : item;
+  const int qt = (CAUSAL && !SPLIT) ? ((PAIR && pass != 0) ? item : n_qtiles - 1 - item) : item;
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;
@@ -341,18 +344,18 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   }
 }
 
-template <int D, int BC, int W, int STAGES, bool CAUSAL>
+template <int D, int BC, int W, int STAGES, bool CAUSAL, bool PAIR = true>
 hipError_t launch_fwd_dl(const FwdParams& p) {
   constexpr int BR = W * 32;
   const int n_qtiles = (p.N + BR - 1) / BR;
-  const long long grid = (long long)p.B * p.H * (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
+  const long long grid = (long long)p.B * p.H * ((CAUSAL && PAIR) ? (n_qtiles + 1) / 2 : n_qtiles);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
   const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
   const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
   (void)hipGetLastError();
-  hipLaunchKernelGGL((fwd_dl_kernel<D, BC, W, STAGES, CAUSAL>), dim3((unsigned)grid), dim3(W * 64), 0,
+  hipLaunchKernelGGL((fwd_dl_kernel<D, BC, W, STAGES, CAUSAL, false, PAIR>), dim3((unsigned)grid), dim3(W * 64), 0,
                      p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
                      (uint16_t*)p.o, p.lse, p.H, p.N, n_qtiles, (int)grid, c, q_and, q_xor);
   return hipGetLastError();
@@ -690,7 +693,8 @@ hipError_t launch_split_t(const FwdParams& p) {
 hipError_t launch_fwd(const FwdParams& p) {
   // Tile shapes (K/V tile 64 keys; 8 waves = 256-row Q tiles, or 4 waves =
   // 128 rows) chosen by measurement on MI355X, each parity-tested.  Causal
-  // grids of fewer than two 8-wave workgroups per CU use the 4-wave tiles.
+  // grids of fewer than two 8-wave workgroups per CU use the 4-wave tiles,
+  // and grids of fewer 4-wave pairs than CUs drop the pairing.
   constexpr int kCus = 256;
   if (!p.causal) {
     // d = 128: the software-pipelined kernel (the VALU work of one tile under
@@ -698,10 +702,14 @@ hipError_t launch_fwd(const FwdParams& p) {
     return p.d == 64 ? launch_fwd_dl<64, 64, 8, 2, false>(p) : launch_fwd_sp<128, 64, 8>(p);
   }
   const long long pairs8 = (long long)p.B * p.H * (((p.N + 255) / 256 + 1) / 2);
+  const long long pairs4 = (long long)p.B * p.H * (((p.N + 127) / 128 + 1) / 2);
   const bool small = pairs8 < 2 * kCus;
+  const bool tiny = pairs4 < kCus;  // 4-wave pairs would leave CUs idle: one tile each
   if (p.d == 64) {
+    if (tiny) return launch_fwd_dl<64, 64, 4, 2, true, false>(p);
     return small ? launch_fwd_dl<64, 64, 4, 2, true>(p) : launch_fwd_dl<64, 64, 8, 2, true>(p);
   }
+  if (tiny) return launch_fwd_dl<128, 64, 4, 2, true, false>(p);
   return small ? launch_fwd_dl<128, 64, 4, 2, true>(p) : launch_fwd_dl<128, 64, 8, 2, true>(p);
 }
 
