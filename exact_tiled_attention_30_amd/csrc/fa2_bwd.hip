@@ -390,9 +390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
       }
       interleave_lds_mfma<2 * (D / 16), 1, 4>();
 
-      // P = exp2(S*c - L*log2e), dS = P * (dP - D); masked entries are 0.
-      // Entry (g, e) is query q0 + 4*hi + C with C = t*32 + 8*g + e, visible
-      // iff lo <= C < hi_lim: two compares against per-lane bounds.
+      // P = exp2(S*c - L*log2e), dS = P * (dP - D)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qr = t * 32 + 8 * g + 4 * hi;
@@ -401,14 +399,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          const int C = t * 32 + 8 * g + e;
-          float pr = fast_exp2(fmaf(s[r], c, -l4[e] * kLog2e));
-          if (need_mask && !(lo <= C && C < hi_lim)) pr = 0.f;
-          s[r] = pr;
-          dp[r] = pr * (dp[r] - d4[e]);
+          s[r] = fast_exp2(fmaf(s[r], c, -l4[e] * kLog2e));
+          dp[r] = s[r] * (dp[r] - d4[e]);
         }
       }
-
+      // Entry (g, e) is query q0 + 4*hi + C with C = t*32 + 8*g + e, visible
+      // iff lo <= C < hi_lim.  Masked entries are set to 0 afterwards, on the
+      // diagonal and ragged steps only; the empty volatile asm keeps this a
+      // branch (the compiler would otherwise turn it into selects evaluated
+      // on every step).
+      if (need_mask) {
+        asm volatile("");
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int C = t * 32 + 8 * (r / 4) + r % 4;
+          if (!(lo <= C && C < hi_lim)) {
+            s[r] = 0.f;
+            dp[r] = 0.f;
+          }
+        }
+      }
       // dV += P^T dO and dK += dS^T Q: B operands dO^T and Q^T read transposed
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
@@ -656,13 +666,21 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
       for (int kt = 0; kt < BC / 32; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(fmaf(s[kt][r], c, -l2));
-          if (need_mask) {
-            const int key = kv0 + kt * 32 + acc_row(r, hi);
-            if (!(key < N && (!CAUSAL || key <= my_q))) pr = 0.f;
-          }
+          const float pr = fast_exp2(fmaf(s[kt][r], c, -l2));
           dp[kt][r] = pr * (dp[kt][r] - dd);
         }
+      // masked entries of dS are set to 0 afterwards, on the diagonal and
+      // ragged tiles only; the empty volatile asm keeps this a branch
+      if (need_mask) {
+        asm volatile("");
+#pragma unroll
+        for (int kt = 0; kt < BC / 32; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kt * 32 + acc_row(r, hi);
+            if (!(key < N && (!CAUSAL || key <= my_q))) dp[kt][r] = 0.f;
+          }
+      }
 
       // dQ^T += K^T dS^T
 #pragma unroll
@@ -883,7 +901,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
           __builtin_amdgcn_sched_barrier(0);
         }
 
-        // P = exp2(S*c - L*log2e), dS = P * (dP - D); masked entries are 0
+        // P = exp2(S*c - L*log2e), dS = P * (dP - D)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qr = t * 32 + 8 * g + 4 * hi;
@@ -892,11 +910,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            const int C = t * 32 + 8 * g + e;
-            float pr = fast_exp2(fmaf(s[r], c, -l4[e] * kLog2e));
-            if (need_mask && !(lo <= C && C < hi_lim)) pr = 0.f;
-            s[r] = pr;
-            dp[r] = pr * (dp[r] - d4[e]);
+            s[r] = fast_exp2(fmaf(s[r], c, -l4[e] * kLog2e));
+            dp[r] = s[r] * (dp[r] - d4[e]);
+          }
+        }
+        // Masked entries (C = t*32 + 8g + e outside [lo, hi_lim)) are set to 0
+        // afterwards, on the diagonal and ragged steps only.  The empty
+        // volatile asm keeps this a branch: the compiler would otherwise
+        // turn it into selects evaluated on every step.
+        if (need_mask) {
+          asm volatile("");
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int C = t * 32 + 8 * (r / 4) + r % 4;
+            if (!(lo <= C && C < hi_lim)) {
+              s[r] = 0.f;
+              dp[r] = 0.f;
+            }
           }
         }
 
