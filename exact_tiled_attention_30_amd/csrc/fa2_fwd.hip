@@ -692,14 +692,17 @@ hipError_t launch_split_t(const FwdParams& p) {
 
 hipError_t launch_fwd(const FwdParams& p) {
   // Tile shapes (K/V tile 64 keys; 8 waves = 256-row Q tiles, or 4 waves =
-  // 128 rows) chosen by measurement on MI355X, each parity-tested.  Causal
-  // grids of fewer than two 8-wave workgroups per CU use the 4-wave tiles,
-  // and grids of fewer 4-wave pairs than CUs drop the pairing.
+  // 128 rows) chosen by measurement on MI355X, each parity-tested.  Grids of
+  // fewer 8-wave Q tiles than CUs use 4-wave tiles (twice the workgroups);
+  // causal grids of fewer than two 8-wave workgroups per CU use the 4-wave
+  // tiles too, and grids of fewer 4-wave pairs than CUs drop the pairing.
   constexpr int kCus = 256;
   if (!p.causal) {
     // d = 128: the software-pipelined kernel (the VALU work of one tile under
     // the MFMAs of the next); at d = 64 the plain kernel measures faster
-    return p.d == 64 ? launch_fwd_dl<64, 64, 8, 2, false>(p) : launch_fwd_sp<128, 64, 8>(p);
+    const bool tiny = (long long)p.B * p.H * ((p.N + 255) / 256) < kCus;
+    if (p.d == 64) return tiny ? launch_fwd_dl<64, 64, 4, 2, false>(p) : launch_fwd_dl<64, 64, 8, 2, false>(p);
+    return tiny ? launch_fwd_sp<128, 64, 4>(p) : launch_fwd_sp<128, 64, 8>(p);
   }
   const long long pairs8 = (long long)p.B * p.H * (((p.N + 255) / 256 + 1) / 2);
   const long long pairs4 = (long long)p.B * p.H * (((p.N + 127) / 128 + 1) / 2);

@@ -161,22 +161,27 @@ def test_full_size_workloads_sampled_rows(w):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("N", [600, 192, 100])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_causal_wide_grid_ragged(d):
-    # Enough heads that the causal grid takes 256-row Q tiles, each workgroup
-    # running a heavy and a light tile (or the middle tile alone); N ragged.
-    B, H, N = 2, 128, 600
-    print(f"[fwd causal wide] B={B} H={H} N={N} d={d}", flush=True)
+def test_wide_grid_ragged(d, causal, N):
+    # Enough heads for the grid to fill the CUs, so the 8-wave (256-row) Q
+    # tiles run: non-causal, and causal N=600 with each workgroup running a
+    # heavy and a light tile (or the middle tile alone).  The small shapes
+    # above take the 4-wave tiles of small grids.  Each N ends the K/V loop
+    # differently: ragged tail, two full tiles, one short tile.
+    B, H = 2, 128
+    print(f"[fwd wide] B={B} H={H} N={N} d={d} causal={causal}", flush=True)
     x = make_inputs(B, H, N, d, seed=13)
     d_ = _dev(x)
     o = torch.empty_like(d_["q"])
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    binding.fa2_fwd(d_["q"], d_["k"], d_["v"], o, lse, True, d ** -0.5)
+    binding.fa2_fwd(d_["q"], d_["k"], d_["v"], o, lse, causal, d ** -0.5)
     torch.cuda.synchronize()
     del d_
     every = [(b, h, i) for (b, h) in ((0, 0), (1, 127)) for i in range(N)]
     rows = np.concatenate([np.array(every, dtype=np.int64), sample_rows(B, H, N, seed=3)])
-    o_ref, lse_ref = oracle.attention_forward_rows(x["q"], x["k"], x["v"], True, d ** -0.5, rows)
+    o_ref, lse_ref = oracle.attention_forward_rows(x["q"], x["k"], x["v"], causal, d ** -0.5, rows)
     b, h, i = (torch.as_tensor(rows[:, c], device="cuda") for c in range(3))
     rep = forward_report(o[b, i, h].cpu(), lse[b, h, i].cpu(), o_ref, lse_ref)
     print(f"  {rep}", flush=True)
