@@ -13,6 +13,7 @@
 namespace {
 
 constexpr size_t kMaxElems = (size_t)1 << 62;
+constexpr long long kMaxTokenElems = 1LL << 23;  // H * d of one token
 constexpr int kMaxSplits = 64;  // split-KV slices per Q tile
 
 struct Range {
@@ -37,6 +38,9 @@ int check_shape(int B, int H, int N, int d, float scale, size_t* elems, size_t* 
   if (e > (long double)kMaxElems) return FA2_ERR_SHAPE;
   // every launch size derived from the row count must fit 32-bit grids
   if ((long double)B * H * N > 2147483647.0L) return FA2_ERR_SHAPE;
+  // the kernels address rows within a tile of up to 128 tokens with 32-bit
+  // offsets: 128 tokens of H*d bf16 elements must stay below 2^31 bytes
+  if ((long long)H * d > kMaxTokenElems) return FA2_ERR_SHAPE;
   // grid = B * H * ceil(N / 128) workgroups must fit the launch limit
   const long double grid = (long double)B * H * ((N + 127) / 128);
   if (grid > 2147483647.0L) return FA2_ERR_SHAPE;
@@ -63,7 +67,7 @@ const char* fa2_status_string(int status) {
   switch (status) {
     case FA2_OK: return "FA2_OK";
     case FA2_ERR_NULLPTR: return "FA2_ERR_NULLPTR: a required pointer is NULL";
-    case FA2_ERR_SHAPE: return "FA2_ERR_SHAPE: negative or too large B, H or N";
+    case FA2_ERR_SHAPE: return "FA2_ERR_SHAPE: negative or too large B, H or N, or H*d above 2^23";
     case FA2_ERR_HEADDIM: return "FA2_ERR_HEADDIM: head dimension must be 64 or 128";
     case FA2_ERR_SCALE: return "FA2_ERR_SCALE: scale must be finite";
     case FA2_ERR_ALIGN: return "FA2_ERR_ALIGN: tensor base pointer misaligned";

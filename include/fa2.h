@@ -47,7 +47,8 @@ extern "C" {
 typedef enum fa2_status {
   FA2_OK = 0,
   FA2_ERR_NULLPTR = 1,   /* a required pointer is NULL and the problem is non-empty */
-  FA2_ERR_SHAPE = 2,     /* B, H or N negative, or B*H*N exceeds 2^31 - 1         */
+  FA2_ERR_SHAPE = 2,     /* B, H or N negative, B*H*N exceeds 2^31 - 1, or H*d    */
+                         /* (elements of one token) exceeds 2^23                  */
   FA2_ERR_HEADDIM = 3,   /* d is not 64 or 128                                    */
   FA2_ERR_SCALE = 4,     /* scale is NaN or infinite                              */
   FA2_ERR_ALIGN = 5,     /* a base pointer is not 16-byte (lse: 4-byte) aligned   */

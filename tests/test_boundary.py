@@ -76,6 +76,12 @@ def test_fwd_argument_errors(L):
     assert fwd(L, lse=LSE + 2) == ALIGN
     # grid would exceed the launch limit
     assert fwd(L, B=1 << 20, H=1 << 10, N=1 << 20) == SHAPE
+    # one token wider than 2^23 elements: in-tile row offsets would leave 32
+    # bits.  At exactly 2^23 the shape passes and the NULL q is what fails.
+    assert fwd(L, B=1, H=(1 << 16) + 1, N=8, d=128) == SHAPE
+    assert fwd(L, B=1, H=(1 << 17) + 1, N=8, d=64) == SHAPE
+    assert fwd(L, q=None, B=1, H=1 << 16, N=8, d=128) == NULLPTR
+    assert fwd(L, q=None, B=1, H=1 << 17, N=8, d=64) == NULLPTR
 
 
 def test_fwd_aliasing_is_rejected(L):
