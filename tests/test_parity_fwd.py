@@ -78,6 +78,29 @@ def test_unusual_scales(scale, causal, d):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_nan_in_one_query_row_stays_in_that_row(causal, d):
+    # Non-finite inputs propagate; the pages fix no more than that.  A NaN in
+    # query row i enters only the scores of row i, so exactly that row's O
+    # and L are NaN and every other row still matches the oracle.
+    B, H, N = 1, 2, 300
+    x = make_inputs(B, H, N, d, seed=12)
+    bad = (0, 130, 1)  # (b, i, h): past the first Q tile, inside the second
+    x["q"][bad[0], bad[1], bad[2], 7] = float("nan")
+    print(f"[fwd nan row] d={d} causal={causal}", flush=True)
+    o, lse = run_fwd(x, causal, d ** -0.5)
+    o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal, d ** -0.5)
+    o, lse = o.double().numpy(), lse.numpy().astype(np.float64)
+    assert np.isnan(o[bad[0], bad[1], bad[2]]).all() and np.isnan(lse[bad[0], bad[2], bad[1]])
+    keep = np.ones((B, N, H), dtype=bool)
+    keep[bad] = False
+    rep = forward_report(o[keep], lse.transpose(0, 2, 1)[keep], o_ref[keep],
+                         lse_ref.transpose(0, 2, 1)[keep])
+    print(f"  {rep}", flush=True)
+    assert rep["ok"], rep
+
+
 def test_empty_problem_is_a_noop():
     q = torch.empty((2, 0, 3, 64), dtype=torch.bfloat16, device="cuda")
     o, lse = binding.attention_forward(q, q, q, True, 0.125)
