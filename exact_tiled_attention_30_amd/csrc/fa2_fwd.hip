@@ -9,9 +9,11 @@
 //  * A workgroup of W waves (64 lanes) owns a Q tile of 32*W rows of one
 //    (batch, head); each wave owns 32 query rows and their softmax rows
 //    outright (no cross-wave merge).  Causal workgroups take a heavy and a
-//    light Q tile in turn so all stream the same number of K/V tiles.  Work
-//    items are renumbered so each XCD runs contiguous Q tiles of the same
-//    heads (shared K/V in its L2).
+//    light Q tile in turn so all stream the same number of K/V tiles, or,
+//    when the whole grid fits on the CUs at once, one Q tile each, dealt to
+//    the CUs so that every CU's tiles add up to the same work.  Work items
+//    are renumbered so each XCD runs contiguous Q tiles of the same heads
+//    (shared K/V in its L2).
 //  * Both products run on v_mfma_f32_32x32x16_bf16 in transposed form:
 //    S^T = K Q^T (A = K rows from LDS, B = Q held in VGPRs for the whole
 //    loop) and O^T = V^T P^T (A = V^T read transposed from LDS, B = P^T
@@ -59,6 +61,25 @@ constexpr float kRescaleSlack = 8.0f;
 // LDS buffers are separate arrays picked at compile time (the tile loop is
 // unrolled by two) so the compiler can tell the in-flight LDS DMA into one
 // buffer from the reads of the other.
+// Causal grids that are resident all at once (one Q tile per workgroup):
+// workgroups are placed round-robin over the XCDs, and on an XCD local
+// workgroup L lands on CU L mod 32 (32 CUs per XCD).  Ranking the XCD's Q
+// tiles by their number of K/V tiles, heaviest first, and dealing them to
+// the CUs in snake order (left to right, then right to left, ...) gives every
+// CU the same total.  The host only selects this with whole heads per XCD
+// (grid % 8 == 0 and (grid / 8) % n_qtiles == 0).  Item 0 of a head is its
+// heaviest Q tile (the kernel reverses the tile order).
+__device__ __forceinline__ int dealt_id(int wg, int grid, int n_qtiles) {
+  constexpr int kXcds = 8, kCusPerXcd = 32;
+  const int per = grid / kXcds;
+  const int xcd = wg % kXcds, local = wg / kXcds;
+  const int round = local / kCusPerXcd, cu = local % kCusPerXcd;
+  const int width = min(kCusPerXcd, per - round * kCusPerXcd);
+  const int rank = round * kCusPerXcd + ((round & 1) ? width - 1 - cu : cu);
+  const int heads = per / n_qtiles;
+  return xcd * per + (rank % heads) * n_qtiles + rank / heads;
+}
+
 template <int D>
 struct DlSwz {
   // XOR applied to the 16-byte chunk index of row r
@@ -72,7 +93,10 @@ struct DlSwz {
 // PAIR (causal): a work item is a heavy + light pair of Q tiles; without it,
 // one Q tile, heaviest first -- for grids too small to fill the GPU, where
 // twice the workgroups beat the balance.
-template <int D, int BC, int W, int STAGES, bool CAUSAL, bool SPLIT = false, bool PAIR = true>
+// DEAL (causal, unpaired): the whole grid is resident at once, so the tiles
+// are dealt to CUs by weight (dealt_id) instead of heaviest first per head.
+template <int D, int BC, int W, int STAGES, bool CAUSAL, bool SPLIT = false, bool PAIR = true,
+          bool DEAL = false>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 1))) void fwd_dl_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -103,7 +127,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   // Work item: non-causal, one Q tile; causal, the pair (n_qtiles-1-p, p)
   // of a heavy and a light Q tile, so every workgroup streams the same
   // number of K/V tiles (n_qtiles + 1 tile rows of keys) whatever p is.
-  const int logical0 = xcd_contiguous_id(blockIdx.x, grid);
+  const int logical0 = DEAL ? dealt_id(blockIdx.x, grid, n_qtiles) : xcd_contiguous_id(blockIdx.x, grid);
   const int split = SPLIT ? logical0 % n_split : 0;  // slices of one Q tile are adjacent
   const int logical = SPLIT ? logical0 / n_split : logical0;
   const int per_head = (CAUSAL && !SPLIT && PAIR) ? (n_qtiles + 1) / 2 : n_qtiles;
@@ -344,7 +368,24 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   }
 }
 
-template <int D, int BC, int W, int STAGES, bool CAUSAL, bool PAIR = true>
+// Workgroups of this kernel one CU holds at once (its occupancy), queried
+// once per process; 0 if the query fails, which turns the dealt path off.
+template <int D, int BC, int W, int STAGES, bool CAUSAL, bool PAIR, bool DEAL>
+int resident_wgs() {
+  static const int n = [] {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, fwd_dl_kernel<D, BC, W, STAGES, CAUSAL, false, PAIR, DEAL>, W * 64, 0) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    return blocks;
+  }();
+  return n;
+}
+
+template <int D, int BC, int W, int STAGES, bool CAUSAL, bool PAIR = true, bool DEAL = false>
 hipError_t launch_fwd_dl(const FwdParams& p) {
   constexpr int BR = W * 32;
   const int n_qtiles = (p.N + BR - 1) / BR;
@@ -355,7 +396,7 @@ hipError_t launch_fwd_dl(const FwdParams& p) {
   const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
   const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
   (void)hipGetLastError();
-  hipLaunchKernelGGL((fwd_dl_kernel<D, BC, W, STAGES, CAUSAL, false, PAIR>), dim3((unsigned)grid), dim3(W * 64), 0,
+  hipLaunchKernelGGL((fwd_dl_kernel<D, BC, W, STAGES, CAUSAL, false, PAIR, DEAL>), dim3((unsigned)grid), dim3(W * 64), 0,
                      p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
                      (uint16_t*)p.o, p.lse, p.H, p.N, n_qtiles, (int)grid, c, q_and, q_xor);
   return hipGetLastError();
@@ -696,6 +737,8 @@ hipError_t launch_fwd(const FwdParams& p) {
   // fewer 8-wave Q tiles than CUs use 4-wave tiles (twice the workgroups);
   // causal grids of fewer than two 8-wave workgroups per CU use the 4-wave
   // tiles too, and grids of fewer 4-wave pairs than CUs drop the pairing.
+  // A causal grid of one 4-wave workgroup per Q tile that the CUs hold all
+  // at once, with whole heads per XCD, is dealt to the CUs by weight.
   constexpr int kCus = 256;
   if (!p.causal) {
     // d = 128: the software-pipelined kernel (the VALU work of one tile under
@@ -705,13 +748,22 @@ hipError_t launch_fwd(const FwdParams& p) {
     return tiny ? launch_fwd_sp<128, 64, 4>(p) : launch_fwd_sp<128, 64, 8>(p);
   }
   const long long pairs8 = (long long)p.B * p.H * (((p.N + 255) / 256 + 1) / 2);
-  const long long pairs4 = (long long)p.B * p.H * (((p.N + 127) / 128 + 1) / 2);
+  const long long nq4 = (p.N + 127) / 128;
+  const long long pairs4 = (long long)p.B * p.H * ((nq4 + 1) / 2);
+  const long long tiles4 = (long long)p.B * p.H * nq4;
   const bool small = pairs8 < 2 * kCus;
   const bool tiny = pairs4 < kCus;  // 4-wave pairs would leave CUs idle: one tile each
+  // one 4-wave workgroup per Q tile, all resident at once, dealt to the CUs
+  // by weight: twice the waves of the pairs, with the same balance
+  const bool whole_heads = tiles4 % 8 == 0 && (tiles4 / 8) % nq4 == 0;
   if (p.d == 64) {
+    if (whole_heads && tiles4 <= (long long)kCus * resident_wgs<64, 64, 4, 2, true, false, true>())
+      return launch_fwd_dl<64, 64, 4, 2, true, false, true>(p);
     if (tiny) return launch_fwd_dl<64, 64, 4, 2, true, false>(p);
     return small ? launch_fwd_dl<64, 64, 4, 2, true>(p) : launch_fwd_dl<64, 64, 8, 2, true>(p);
   }
+  if (whole_heads && tiles4 <= (long long)kCus * resident_wgs<128, 64, 4, 2, true, false, true>())
+    return launch_fwd_dl<128, 64, 4, 2, true, false, true>(p);
   if (tiny) return launch_fwd_dl<128, 64, 4, 2, true, false>(p);
   return small ? launch_fwd_dl<128, 64, 4, 2, true>(p) : launch_fwd_dl<128, 64, 8, 2, true>(p);
 }

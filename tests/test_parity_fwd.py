@@ -49,6 +49,11 @@ SMALL_SHAPES = [
     (2, 1, 200, 128),
     (1, 1, 192, 128),
     (1, 1, 63, 128),
+    # causal grids with whole heads on each XCD run one Q tile per workgroup
+    # dealt to the CUs by weight
+    (2, 4, 1024, 64),
+    (2, 4, 1000, 64),
+    (1, 8, 1000, 128),
 ]
 
 
