@@ -68,7 +68,9 @@ constexpr float kRescaleSlack = 8.0f;
 // the CUs in snake order (left to right, then right to left, ...) gives every
 // CU the same total.  The host only selects this with whole heads per XCD
 // (grid % 8 == 0 and (grid / 8) % n_qtiles == 0).  Item 0 of a head is its
-// heaviest Q tile (the kernel reverses the tile order).
+// heaviest Q tile (the kernel reverses the tile order).  On a grid larger
+// than the CUs hold, the first round is placed as above and the later
+// workgroups, dispatched in rank order, take whichever slot frees first.
 __device__ __forceinline__ int dealt_id(int wg, int grid, int n_qtiles) {
   constexpr int kXcds = 8, kCusPerXcd = 32;
   const int per = grid / kXcds;
@@ -737,8 +739,9 @@ hipError_t launch_fwd(const FwdParams& p) {
   // fewer 8-wave Q tiles than CUs use 4-wave tiles (twice the workgroups);
   // causal grids of fewer than two 8-wave workgroups per CU use the 4-wave
   // tiles too, and grids of fewer 4-wave pairs than CUs drop the pairing.
-  // A causal grid of one 4-wave workgroup per Q tile that the CUs hold all
-  // at once, with whole heads per XCD, is dealt to the CUs by weight.
+  // Causal grids with whole heads per XCD run one 4-wave workgroup per Q
+  // tile, dealt to the CUs by weight (d = 128: only when the CUs hold the
+  // whole grid at once).
   constexpr int kCus = 256;
   if (!p.causal) {
     // d = 128: the software-pipelined kernel (the VALU work of one tile under
@@ -753,12 +756,16 @@ hipError_t launch_fwd(const FwdParams& p) {
   const long long tiles4 = (long long)p.B * p.H * nq4;
   const bool small = pairs8 < 2 * kCus;
   const bool tiny = pairs4 < kCus;  // 4-wave pairs would leave CUs idle: one tile each
-  // one 4-wave workgroup per Q tile, all resident at once, dealt to the CUs
-  // by weight: twice the waves of the pairs, with the same balance
+  // One 4-wave workgroup per Q tile, dealt to the CUs by weight: twice the
+  // waves of the pairs with the same balance when the grid is resident at
+  // once; on larger grids the first round is dealt the same way and later
+  // workgroups, still heaviest first, go wherever a slot frees.  At d = 64
+  // that beats the pairs on every causal workload measured (1-5 % past one
+  // round); at d = 128 only within one round (past it, 4-5 % slower at
+  // N >= 8192).
   const bool whole_heads = tiles4 % 8 == 0 && (tiles4 / 8) % nq4 == 0;
   if (p.d == 64) {
-    if (whole_heads && tiles4 <= (long long)kCus * resident_wgs<64, 64, 4, 2, true, false, true>())
-      return launch_fwd_dl<64, 64, 4, 2, true, false, true>(p);
+    if (whole_heads) return launch_fwd_dl<64, 64, 4, 2, true, false, true>(p);
     if (tiny) return launch_fwd_dl<64, 64, 4, 2, true, false>(p);
     return small ? launch_fwd_dl<64, 64, 4, 2, true>(p) : launch_fwd_dl<64, 64, 8, 2, true>(p);
   }
