@@ -212,6 +212,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
   float m_run = -INFINITY;
+  float m_thr = -INFINITY;  // m_run + kRescaleSlack
+  float neg_mref = 0.f;     // -m_run, or 0 while m_run is -inf
   float l_part = 0.f;
 
   auto tile = [&](int jt, const uint8_t* kb, const uint8_t* vb) __attribute__((always_inline)) {
@@ -241,27 +243,29 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
 
     const bool need_mask = (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N);
     if (need_mask) {
+      // key kv0 + kt*32 + acc_row(r, hi) is visible iff it is below N and, if
+      // causal, at most my_q: iff kt*32 + acc_row(r, 0) <= lim, a compile-time
+      // constant against one per-lane bound
+      const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - kv0 - 4 * hi;
 #pragma unroll
       for (int kt = 0; kt < BC / 32; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kt * 32 + acc_row(r, hi);
-          const bool visible = key < N && (!CAUSAL || key <= my_q);
-          if (!visible) s[kt][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kt * 32 + acc_row(r, 0) > lim) s[kt][r] = -INFINITY;
     }
     float mx = lane_max<BC / 2>(s);
     mx = pair_max(mx);
-    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-    if (wave_any(mt > m_run + kRescaleSlack)) {
+    const float mt = mx * c;  // c > 0: a row with no visible key stays -inf
+    if (wave_any(mt > m_thr)) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
       l_part *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
+      m_thr = m_run + kRescaleSlack;
+      neg_mref = (m_run == -INFINITY) ? 0.f : -m_run;
     }
-    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
 
     // V^T fragment addresses: this lane supplies row 16*cc + 8*u + 4*hi + i,
     // columns dt*32 + 16*(g%2) + 4*a .. +3 (g = lane/16, i = (lane%16)/4, a = lane%4)
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
       f32x8 p8;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        p8[t] = fast_exp2(fmaf(sv[r0 + t], c, -mref));
+        p8[t] = fast_exp2(fmaf(sv[r0 + t], c, neg_mref));
         rs += p8[t];
       }
       const bf16x8 pcur = to_bf16x8(p8);
@@ -509,35 +513,40 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
   auto tile_max = [&](const f32x16* s) __attribute__((always_inline)) {
     float mx = lane_max<BC / 2>(s);
     mx = pair_max(mx);
-    return (mx == -INFINITY) ? -INFINITY : mx * c;
+    return mx * c;  // c > 0: a row with no visible key stays -inf
   };
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
   float m_run = -INFINITY;
+  float m_thr = -INFINITY;  // m_run + kRescaleSlack
+  float neg_mref = 0.f;     // -m_run, or 0 while m_run is -inf
   float l_part = 0.f;
-  // lazy rescale (see fwd_dl_kernel); returns the reference the tile's P uses
+  // lazy rescale (see fwd_dl_kernel); returns minus the reference the tile's
+  // P uses
   auto rescale_to = [&](float mt) __attribute__((always_inline)) {
-    if (wave_any(mt > m_run + kRescaleSlack)) {
+    if (wave_any(mt > m_thr)) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
       l_part *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
+      m_thr = m_run + kRescaleSlack;
+      neg_mref = (m_run == -INFINITY) ? 0.f : -m_run;
     }
-    return (m_run == -INFINITY) ? 0.f : m_run;
+    return neg_mref;
   };
   // P = exp2(S c - mref) in bf16, and its fp32 row sum
-  auto probs = [&](const f32x16* sc, float mref, bf16x8* pf) __attribute__((always_inline)) {
+  auto probs = [&](const f32x16* sc, float nm, bf16x8* pf) __attribute__((always_inline)) {
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int cc = 0; cc < BC / 16; ++cc) {
       f32x8 p8;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        p8[t] = fast_exp2(fmaf(sc[cc / 2][8 * (cc % 2) + t], c, -mref));
+        p8[t] = fast_exp2(fmaf(sc[cc / 2][8 * (cc % 2) + t], c, nm));
         if (t % 2) rs1 += p8[t];
         else rs0 += p8[t];
       }
@@ -586,10 +595,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
                   uint8_t* k_dma, uint8_t* v_dma) __attribute__((always_inline)) {
     if (jt + 2 < n_kv) issue_one(k, koff, jt + 2, k_dma);
     issue_one(v, voff, jt + 1, v_dma);
-    const float mref = rescale_to(mt);
+    const float nm = rescale_to(mt);
     bf16x8 pf[BC / 16];
     scores(k_next, sn);
-    const float rs = probs(sc, mref, pf);
+    const float rs = probs(sc, nm, pf);
     pv(v_cur, pf);
     mt = tile_max(sn);
     l_part += rs;
@@ -601,9 +610,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
       __attribute__((always_inline)) {
     if (jt + 2 < n_kv) issue_one(k, koff, jt + 2, k_dma);
     if (jt + 1 < n_kv) issue_one(v, voff, jt + 1, v_dma);
-    const float mref = rescale_to(mt);
+    const float nm = rescale_to(mt);
     bf16x8 pf[BC / 16];
-    const float rs = probs(sc, mref, pf);
+    const float rs = probs(sc, nm, pf);
     pv(v_cur, pf);
     l_part += rs;
     wait_dma_and_lds();
@@ -634,9 +643,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (kv0 + kt * 32 + acc_row(r, hi) >= N) st[kt][r] = -INFINITY;
-    const float mref = rescale_to(tile_max(st));
+    const float nm = rescale_to(tile_max(st));
     bf16x8 pf[BC / 16];
-    const float rs = probs(st, mref, pf);
+    const float rs = probs(st, nm, pf);
     pv(vc, pf);
     l_part += rs;
   }
