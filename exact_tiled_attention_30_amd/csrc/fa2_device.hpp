@@ -60,18 +60,24 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, kWave);
 }
 
-// Max of a lane's scores, written with fmaxf so the compiler forms the
-// v_max3_f32 chain itself.  It must stay compiler-visible: the hazard
+// Max of a lane's scores.  It must stay compiler-visible: the hazard
 // recognizer pads a VALU read of an MFMA result only when it can see the
 // instruction, and a hand-written v_max reading an accumulator right after
 // its MFMA was observed to see a partial sum (a race that only moved the
 // lazy-rescale reference, so results differed from run to run by rounding).
-// NaN handling is IEEE (the compiler canonicalises the first pair).
+// The NaN-propagating maximum lowers to a v_maximum3_f32 chain on gfx950
+// with no operand canonicalisation (fmaxf's IEEE maxNum quiets the first
+// operands with extra v_max instructions).  A NaN score makes the row max
+// NaN, which never triggers a rescale; that row's P, l and O are NaN anyway.
+__device__ __forceinline__ float fmax_nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
 template <int NV>
 __device__ __forceinline__ float lane_max(const f32x16* s) {
-  float mx = fmaxf(s[0][0], s[0][1]);
+  float mx = fmax_nan(s[0][0], s[0][1]);
 #pragma unroll
-  for (int i = 2; i < NV; i += 2) mx = fmaxf(fmaxf(mx, s[i / 16][i % 16]), s[i / 16][i % 16 + 1]);
+  for (int i = 2; i < NV; i += 2)
+    mx = fmax_nan(fmax_nan(mx, s[i / 16][i % 16]), s[i / 16][i % 16 + 1]);
   return mx;
 }
 
@@ -82,7 +88,7 @@ __device__ __forceinline__ float lane_max(const f32x16* s) {
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
