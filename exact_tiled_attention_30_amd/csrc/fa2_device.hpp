@@ -116,11 +116,35 @@ __device__ __forceinline__ void wait_dma_and_lds() { __builtin_amdgcn_s_waitcnt(
 // i % 8).  Renumber them so that each XCD receives one contiguous range of
 // logical ids; consecutive logical ids are Q tiles of the same (batch, head),
 // which then share K/V through that XCD's L2.  Bijective for any grid size.
-__device__ __forceinline__ int xcd_contiguous_id(int wg, int grid) {
+// Host-callable so the map can be checked on the CPU.
+__host__ __device__ inline int xcd_contiguous_id(int wg, int grid) {
   constexpr int kXcds = 8;
   const int per = grid / kXcds, rem = grid % kXcds;
   const int xcd = wg % kXcds, slot = wg / kXcds;
   return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
+// Causal grids that are resident all at once (one Q tile per workgroup):
+// workgroups are placed round-robin over the XCDs, and on an XCD local
+// workgroup L lands on CU L mod 32 (32 CUs per XCD).  Ranking the XCD's Q
+// tiles by their number of K/V tiles, heaviest first, and dealing them to
+// the CUs in snake order (left to right, then right to left, ...) gives every
+// CU the same total.  The host only selects this with whole heads per XCD
+// (grid % 8 == 0 and (grid / 8) % n_qtiles == 0).  Item 0 of a head is its
+// heaviest Q tile (the kernel reverses the tile order).  On a grid larger
+// than the CUs hold, the first round is placed as above and the later
+// workgroups, dispatched in rank order, take whichever slot frees first.
+// Host-callable so the map can be checked on the CPU.
+__host__ __device__ inline int dealt_id(int wg, int grid, int n_qtiles) {
+  constexpr int kXcds = 8, kCusPerXcd = 32;
+  const int per = grid / kXcds;
+  const int xcd = wg % kXcds, local = wg / kXcds;
+  const int round = local / kCusPerXcd, cu = local % kCusPerXcd;
+  const int left = per - round * kCusPerXcd;
+  const int width = left < kCusPerXcd ? left : kCusPerXcd;
+  const int rank = round * kCusPerXcd + ((round & 1) ? width - 1 - cu : cu);
+  const int heads = per / n_qtiles;
+  return xcd * per + (rank % heads) * n_qtiles + rank / heads;
 }
 
 }  // namespace fa2

@@ -61,27 +61,6 @@ constexpr float kRescaleSlack = 8.0f;
 // LDS buffers are separate arrays picked at compile time (the tile loop is
 // unrolled by two) so the compiler can tell the in-flight LDS DMA into one
 // buffer from the reads of the other.
-// Causal grids that are resident all at once (one Q tile per workgroup):
-// workgroups are placed round-robin over the XCDs, and on an XCD local
-// workgroup L lands on CU L mod 32 (32 CUs per XCD).  Ranking the XCD's Q
-// tiles by their number of K/V tiles, heaviest first, and dealing them to
-// the CUs in snake order (left to right, then right to left, ...) gives every
-// CU the same total.  The host only selects this with whole heads per XCD
-// (grid % 8 == 0 and (grid / 8) % n_qtiles == 0).  Item 0 of a head is its
-// heaviest Q tile (the kernel reverses the tile order).  On a grid larger
-// than the CUs hold, the first round is placed as above and the later
-// workgroups, dispatched in rank order, take whichever slot frees first.
-__device__ __forceinline__ int dealt_id(int wg, int grid, int n_qtiles) {
-  constexpr int kXcds = 8, kCusPerXcd = 32;
-  const int per = grid / kXcds;
-  const int xcd = wg % kXcds, local = wg / kXcds;
-  const int round = local / kCusPerXcd, cu = local % kCusPerXcd;
-  const int width = min(kCusPerXcd, per - round * kCusPerXcd);
-  const int rank = round * kCusPerXcd + ((round & 1) ? width - 1 - cu : cu);
-  const int heads = per / n_qtiles;
-  return xcd * per + (rank % heads) * n_qtiles + rank / heads;
-}
-
 template <int D>
 struct DlSwz {
   // XOR applied to the 16-byte chunk index of row r
