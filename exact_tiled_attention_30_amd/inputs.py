@@ -78,6 +78,23 @@ def make_inputs(B: int, H: int, N: int, d: int, seed: int = 0,
     return out
 
 
+def make_inputs_on_device(B: int, H: int, N: int, d: int, seed: int = 0,
+                          with_dout: bool = False, device: str = "cuda"):
+    """The same recipe as make_inputs -- N(0,1) fp32 draws rounded to bf16, in
+    the order q, k, v (, dout) -- but drawn by torch's generator on the device,
+    one batch entry at a time, for tensors too large to draw on the host.  The
+    values differ from make_inputs' for the same seed (another generator)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    out = {}
+    for name in ("q", "k", "v") + (("dout",) if with_dout else ()):
+        t = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=device)
+        for b in range(B):
+            t[b] = torch.randn((N, H, d), generator=g, dtype=torch.float32,
+                               device=device).to(torch.bfloat16)
+        out[name] = t
+    return out
+
+
 def inputs_for(w: Workload):
     return make_inputs(w.B, w.H, w.N, w.d, seed=w.seed,
                        peaked_fraction=w.peaked_fraction, with_dout=w.backward)

@@ -1,0 +1,82 @@
+"""GPU parity past 32-bit offsets.
+
+Tensors of B*N*H*d > 2^31 elements (5.4 GB of bf16 each) put element indices
+above 2^31 and byte offsets above 2^32, which every address computation of
+the kernels must carry in 64 bits.  Forward (both masks) and the two-pass
+backward run on the whole tensors; the fp64 oracle checks sampled rows of
+heads at the far end of the tensors (and one in the middle) for the
+forward, and whole heads for the backward, on exact host copies of those
+heads' inputs.  Inputs come from the device generator of the input module
+(the same N(0,1) -> bf16 recipe): drawing 5.4 GB tensors on the host would
+take minutes.  About 50 GB of device memory.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_tiled_attention_30_amd import binding
+from exact_tiled_attention_30_amd.inputs import make_inputs_on_device
+from oracle.compare import forward_report, gradient_report
+
+pytestmark = pytest.mark.gpu
+
+B, H, N, D = 80, 64, 4096, 128
+HEADS = [(B - 1, H - 1), (B - 1, 0), (B // 2 + 3, 17)]
+
+
+def head(t, b, h):
+    """One head of a [B, N, H, d] device tensor as a [1, N, 1, d] host tensor."""
+    return t[b:b + 1, :, h:h + 1, :].cpu()
+
+
+@pytest.fixture(scope="module")
+def big():
+    assert B * N * H * D > 2 ** 31
+    free, _ = torch.cuda.mem_get_info()
+    if free < 60e9:
+        pytest.skip(f"needs about 50 GB of free device memory, {free / 1e9:.1f} GB free")
+    print(f"[large] B={B} H={H} N={N} d={D}: {B * N * H * D * 2 / 1e9:.2f} GB per tensor",
+          flush=True)
+    x = make_inputs_on_device(B, H, N, D, seed=11, with_dout=True)
+    yield x
+    del x
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_forward_past_32bit_offsets(big, causal):
+    scale = D ** -0.5
+    o, lse = binding.attention_forward(big["q"], big["k"], big["v"], causal, scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    for (b, h) in HEADS:
+        idx = sorted({0, 1, 127, 128, N // 2, N - 2, N - 1, *rng.integers(N, size=9).tolist()})
+        rows = np.array([(0, 0, i) for i in idx], dtype=np.int64)
+        o_ref, lse_ref = oracle.attention_forward_rows(head(big["q"], b, h), head(big["k"], b, h),
+                                                       head(big["v"], b, h), causal, scale, rows)
+        i = torch.as_tensor(idx, device="cuda")
+        rep = forward_report(o[b, i, h].cpu(), lse[b, h, i].cpu(), o_ref, lse_ref)
+        print(f"  head ({b}, {h}) causal={causal}: {rep}", flush=True)
+        assert rep["ok"], ((b, h), rep)
+    del o, lse
+
+
+def test_backward_past_32bit_offsets(big):
+    scale = D ** -0.5
+    causal = True
+    o, lse = binding.attention_forward(big["q"], big["k"], big["v"], causal, scale)
+    dq, dk, dv = binding.attention_backward(big["q"], big["k"], big["v"], o, lse, big["dout"],
+                                            causal, scale)
+    torch.cuda.synchronize()
+    for (b, h) in HEADS[:2]:
+        ref = oracle.attention_backward(head(big["q"], b, h), head(big["k"], b, h),
+                                        head(big["v"], b, h), head(big["dout"], b, h), causal,
+                                        scale)
+        for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+            got = g[b, :, h, :].double().cpu().numpy()[None]
+            rep = gradient_report(got, ref[name])
+            print(f"  head ({b}, {h}) {name}: max_rel={rep['max_rel']:.4f} "
+                  f"mean_rel={rep['mean_rel']:.4f}", flush=True)
+            assert rep["ok"], ((b, h), name, rep)
+    del o, lse, dq, dk, dv
