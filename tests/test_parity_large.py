@@ -2,8 +2,9 @@
 
 Tensors of B*N*H*d > 2^31 elements (5.4 GB of bf16 each) put element indices
 above 2^31 and byte offsets above 2^32, which every address computation of
-the kernels must carry in 64 bits.  Forward (both masks) and the two-pass
-backward run on the whole tensors; the fp64 oracle checks sampled rows of
+the kernels must carry in 64 bits.  The forward (both masks), the split-KV
+and FA-1-order forwards, and both backward strategies run on the whole
+tensors; the fp64 oracle checks sampled rows of
 heads at the far end of the tensors (and one in the middle) for the
 forward, and whole heads for the backward, on exact host copies of those
 heads' inputs.  Inputs come from the device generator of the input module
@@ -44,11 +45,19 @@ def big():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_forward_past_32bit_offsets(big, causal):
+FORWARDS = [("fa2", False), ("fa2", True), ("split_kv", True), ("fa1_order", True)]
+
+
+@pytest.mark.parametrize("algo,causal", FORWARDS, ids=[f"{a}-{'causal' if c else 'full'}"
+                                                       for a, c in FORWARDS])
+def test_forward_past_32bit_offsets(big, algo, causal):
     scale = D ** -0.5
-    o, lse = binding.attention_forward(big["q"], big["k"], big["v"], causal, scale)
+    fwd = {"fa2": binding.attention_forward,
+           "split_kv": lambda q, k, v, c, s: binding.attention_forward_split_kv(q, k, v, c, s, 2),
+           "fa1_order": binding.attention_forward_fa1_order}[algo]
+    o, lse = fwd(big["q"], big["k"], big["v"], causal, scale)
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()  # the split-KV / FA-1-order workspaces
     rng = np.random.default_rng(3)
     for (b, h) in HEADS:
         idx = sorted({0, 1, 127, 128, N // 2, N - 2, N - 1, *rng.integers(N, size=9).tolist()})
@@ -57,18 +66,20 @@ def test_forward_past_32bit_offsets(big, causal):
                                                        head(big["v"], b, h), causal, scale, rows)
         i = torch.as_tensor(idx, device="cuda")
         rep = forward_report(o[b, i, h].cpu(), lse[b, h, i].cpu(), o_ref, lse_ref)
-        print(f"  head ({b}, {h}) causal={causal}: {rep}", flush=True)
+        print(f"  {algo} head ({b}, {h}) causal={causal}: {rep}", flush=True)
         assert rep["ok"], ((b, h), rep)
     del o, lse
 
 
-def test_backward_past_32bit_offsets(big):
+@pytest.mark.parametrize("atomic_dq", [False, True], ids=["two_pass", "atomic_dq"])
+def test_backward_past_32bit_offsets(big, atomic_dq):
     scale = D ** -0.5
     causal = True
     o, lse = binding.attention_forward(big["q"], big["k"], big["v"], causal, scale)
     dq, dk, dv = binding.attention_backward(big["q"], big["k"], big["v"], o, lse, big["dout"],
-                                            causal, scale)
+                                            causal, scale, atomic_dq=atomic_dq)
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     for (b, h) in HEADS[:2]:
         ref = oracle.attention_backward(head(big["q"], b, h), head(big["k"], b, h),
                                         head(big["v"], b, h), head(big["dout"], b, h), causal,
@@ -76,7 +87,7 @@ def test_backward_past_32bit_offsets(big):
         for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
             got = g[b, :, h, :].double().cpu().numpy()[None]
             rep = gradient_report(got, ref[name])
-            print(f"  head ({b}, {h}) {name}: max_rel={rep['max_rel']:.4f} "
+            print(f"  atomic_dq={atomic_dq} head ({b}, {h}) {name}: max_rel={rep['max_rel']:.4f} "
                   f"mean_rel={rep['mean_rel']:.4f}", flush=True)
             assert rep["ok"], ((b, h), name, rep)
     del o, lse, dq, dk, dv
