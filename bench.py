@@ -210,7 +210,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(heads shard with no communication; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
