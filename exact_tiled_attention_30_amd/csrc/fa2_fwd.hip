@@ -555,6 +555,20 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
         oacc[dt] = mfma32(as_bf16x8(u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}), pf[cc],
                           oacc[dt]);
       }
+    {
+      // Schedule of the block this lands in (in a pipelined step: the S
+      // products of the next tile, P of this one and these PV products):
+      // eight LDS reads, then one MFMA per two reads, so the V^T reads are
+      // issued under the S MFMAs instead of just before their own MFMAs
+      constexpr int kM = (BC / 16) * (D / 32), kAhead = 8;
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+      for (int i = 0; i < (2 * kM - kAhead) / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kM - (2 * kM - kAhead) / 2, 0);
+    }
   };
 
   wait_dma_and_lds();  // K(0), V(0), K(1) and Q have landed
