@@ -277,6 +277,19 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
                           oacc[dt]);
       }
     }
+    if constexpr (D == 128) {
+      // eight LDS reads ahead, then one MFMA per two V^T reads (interleaved
+      // A/B on MI355X, causal d = 128: +1.4 to +2.5 % with 8 waves, +3.5 to
+      // +3.9 % with 4; mixed at d = 64)
+      constexpr int kM = (BC / 16) * (D / 32), kAhead = 8;
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+      for (int i = 0; i < (2 * kM - kAhead) / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kM - (2 * kM - kAhead) / 2, 0);
+    }
     l_part += rs;
   };
 
@@ -555,11 +568,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
         oacc[dt] = mfma32(as_bf16x8(u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}), pf[cc],
                           oacc[dt]);
       }
-    {
+    if constexpr (W == 8) {
       // Schedule of the block this lands in (in a pipelined step: the S
       // products of the next tile, P of this one and these PV products):
       // eight LDS reads, then one MFMA per two reads, so the V^T reads are
       // issued under the S MFMAs instead of just before their own MFMAs
+      // (the 4-wave variant measured 13 % slower with it)
       constexpr int kM = (BC / 16) * (D / 32), kAhead = 8;
       __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
