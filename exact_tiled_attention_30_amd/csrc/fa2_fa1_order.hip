@@ -226,9 +226,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void f
 template <int D, bool CAUSAL>
 hipError_t launch_t(const Fa1Params& p) {
   const long long grid = (long long)p.B * p.H;
-  const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
-  const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
-  const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
+  const FwdScale sc = fwd_scale(p.scale);
+  const float c = sc.c;
+  const uint32_t q_and = sc.q_and, q_xor = sc.q_xor;
   (void)hipGetLastError();
   hipLaunchKernelGGL((fa1_order_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(512), 0, p.stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,

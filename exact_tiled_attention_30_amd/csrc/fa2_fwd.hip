@@ -390,9 +390,9 @@ hipError_t launch_fwd_dl(const FwdParams& p) {
   const long long grid = (long long)p.B * p.H * ((CAUSAL && PAIR) ? (n_qtiles + 1) / 2 : n_qtiles);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
-  const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
-  const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
+  const FwdScale sc = fwd_scale(p.scale);
+  const float c = sc.c;
+  const uint32_t q_and = sc.q_and, q_xor = sc.q_xor;
   (void)hipGetLastError();
   hipLaunchKernelGGL((fwd_dl_kernel<D, BC, W, STAGES, CAUSAL, false, PAIR, DEAL>), dim3((unsigned)grid), dim3(W * 64), 0,
                      p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
@@ -680,9 +680,9 @@ hipError_t launch_fwd_sp(const FwdParams& p) {
   const long long grid = (long long)p.B * p.H * n_qtiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
-  const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
-  const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
+  const FwdScale sc = fwd_scale(p.scale);
+  const float c = sc.c;
+  const uint32_t q_and = sc.q_and, q_xor = sc.q_xor;
   (void)hipGetLastError();
   hipLaunchKernelGGL((fwd_sp_kernel<D, BC, W>), dim3((unsigned)grid), dim3(W * 64), 0, p.stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,
@@ -731,9 +731,9 @@ hipError_t launch_split_t(const FwdParams& p) {
   const long long grid = (long long)p.B * p.H * n_qtiles * p.n_split;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const float c = p.scale == 0.f ? 1.0f : (float)(fabs((double)p.scale) * 1.4426950408889634);
-  const uint32_t q_and = p.scale == 0.f ? 0u : 0xffffffffu;
-  const uint32_t q_xor = p.scale < 0.f ? 0x80008000u : 0u;
+  const FwdScale sc = fwd_scale(p.scale);
+  const float c = sc.c;
+  const uint32_t q_and = sc.q_and, q_xor = sc.q_xor;
   (void)hipGetLastError();
   hipLaunchKernelGGL((fwd_dl_kernel<D, 64, W, 2, CAUSAL, true>), dim3((unsigned)grid), dim3(W * 64),
                      0, p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v,

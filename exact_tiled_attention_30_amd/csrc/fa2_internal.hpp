@@ -4,8 +4,33 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa2 {
+
+// Softmax constants of the forward kernels for a given scale: the kernels
+// form exp2(s * c - m) with c = |scale| * log2(e) > 0, flip the bf16 sign bits
+// of Q (exact) for a negative scale, and zero Q (q_and = 0, c = 1) for a zero
+// scale -- or one so small that c is not a normal fp32 number, where every
+// scaled score is 0 to fp32 precision anyway and a zero or subnormal c would
+// turn the masked scores' -inf * c into NaN.
+struct FwdScale {
+  float c;
+  uint32_t q_and, q_xor;
+};
+inline FwdScale fwd_scale(float scale) {
+  const float c = (float)((scale < 0.f ? -(double)scale : (double)scale) * 1.4426950408889634);
+  FwdScale r;
+  r.q_xor = scale < 0.f ? 0x80008000u : 0u;
+  if (c >= 1.17549435e-38f) {  // FLT_MIN, the smallest normal fp32
+    r.c = c;
+    r.q_and = 0xffffffffu;
+  } else {
+    r.c = 1.0f;
+    r.q_and = 0u;
+  }
+  return r;
+}
 
 struct FwdParams {
   const void* q;

@@ -71,7 +71,9 @@ def test_small_shapes_every_element(shape, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1.0 / 128])
+# 1e-40 and -1e-45 are subnormal in fp32 (so is |scale| * log2 e), 1e-38 is
+# the smallest order of magnitude whose |scale| * log2 e is still normal
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1.0 / 128, 1e-40, -1e-45, 1e-38])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_unusual_scales(scale, causal, d):
     B, H, N = 1, 2, 300
@@ -236,7 +238,7 @@ def test_fa1_order_every_element(shape, causal):
     assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.125])
+@pytest.mark.parametrize("scale", [0.0, -0.125, 1e-40])
 def test_fa1_order_unusual_scales(scale):
     B, H, N, d = 1, 2, 300, 64
     x = make_inputs(B, H, N, d, seed=5)
@@ -265,6 +267,18 @@ def test_split_kv_every_element(case, causal):
                                                 n_split)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal, d ** -0.5)
+    rep = forward_report(o.cpu(), lse.cpu(), o_ref, lse_ref)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("scale", [0.0, 1e-40])
+def test_split_kv_zero_and_subnormal_scale(scale):
+    B, H, N, d = 1, 2, 700, 128
+    x = make_inputs(B, H, N, d, seed=23)
+    dx = _dev(x)
+    o, lse = binding.attention_forward_split_kv(dx["q"], dx["k"], dx["v"], True, scale, 3)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], True, scale)
     rep = forward_report(o.cpu(), lse.cpu(), o_ref, lse_ref)
     assert rep["ok"], rep
 
