@@ -33,7 +33,9 @@ bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 int check_shape(int B, int H, int N, int d, float scale, size_t* elems, size_t* rows) {
   if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
   if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
-  if (!isfinite(scale)) return FA2_ERR_SCALE;
+  // the kernels work with scale * log2(e), which must be a finite fp32 too
+  if (!isfinite(scale) || !isfinite((float)((double)scale * 1.4426950408889634)))
+    return FA2_ERR_SCALE;
   const long double e = (long double)B * H * N * d;
   if (e > (long double)kMaxElems) return FA2_ERR_SHAPE;
   // every launch size derived from the row count must fit 32-bit grids
@@ -69,7 +71,7 @@ const char* fa2_status_string(int status) {
     case FA2_ERR_NULLPTR: return "FA2_ERR_NULLPTR: a required pointer is NULL";
     case FA2_ERR_SHAPE: return "FA2_ERR_SHAPE: negative or too large B, H or N, or H*d above 2^23";
     case FA2_ERR_HEADDIM: return "FA2_ERR_HEADDIM: head dimension must be 64 or 128";
-    case FA2_ERR_SCALE: return "FA2_ERR_SCALE: scale must be finite";
+    case FA2_ERR_SCALE: return "FA2_ERR_SCALE: scale and scale*log2(e) must be finite fp32 values";
     case FA2_ERR_ALIGN: return "FA2_ERR_ALIGN: tensor base pointer misaligned";
     case FA2_ERR_ALIAS: return "FA2_ERR_ALIAS: an output overlaps another tensor";
     case FA2_ERR_WORKSPACE: return "FA2_ERR_WORKSPACE: workspace missing or too small";

@@ -23,7 +23,8 @@
  *  - L (lse): float32, [B, H, N] contiguous; natural-log logsumexp of the
  *    scaled, masked scores of each query row.
  *  - d must be 64 or 128.  B, H, N >= 0; B*H*N == 0 is a successful no-op.
- *  - scale: any finite float (usually 1/sqrt(d)).
+ *  - scale: any finite float with |scale| * log2(e) finite in fp32, i.e.
+ *    |scale| <= 2.35e38 (usually 1/sqrt(d)).
  *  - Every pointer is a DEVICE pointer owned by the caller; the library keeps
  *    no reference after the call returns and allocates no device memory.
  *    Tensor base pointers must be 16-byte aligned (lse 4-byte aligned).
@@ -50,7 +51,7 @@ typedef enum fa2_status {
   FA2_ERR_SHAPE = 2,     /* B, H or N negative, B*H*N exceeds 2^31 - 1, or H*d    */
                          /* (elements of one token) exceeds 2^23                  */
   FA2_ERR_HEADDIM = 3,   /* d is not 64 or 128                                    */
-  FA2_ERR_SCALE = 4,     /* scale is NaN or infinite                              */
+  FA2_ERR_SCALE = 4,     /* scale is NaN or infinite, or |scale| > 2.35e38        */
   FA2_ERR_ALIGN = 5,     /* a base pointer is not 16-byte (lse: 4-byte) aligned   */
   FA2_ERR_ALIAS = 6,     /* an output range overlaps an input or another output   */
   FA2_ERR_WORKSPACE = 7, /* backward workspace missing or smaller than required   */

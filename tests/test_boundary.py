@@ -69,6 +69,11 @@ def test_fwd_argument_errors(L):
     assert fwd(L, d=0) == HEADDIM
     assert fwd(L, scale=math.inf) == SCALE
     assert fwd(L, scale=math.nan) == SCALE
+    # finite, but scale * log2(e) overflows fp32
+    assert fwd(L, scale=3.0e38) == SCALE
+    assert fwd(L, scale=-3.0e38) == SCALE
+    # 2.3e38 * log2(e) is still finite: the shape checks pass and the NULL q fails
+    assert fwd(L, q=None, scale=2.3e38) == NULLPTR
     for name in ("q", "k", "v", "o", "lse"):
         assert fwd(L, **{name: None}) == NULLPTR, name
     for name in ("q", "k", "v", "o"):
