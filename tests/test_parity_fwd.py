@@ -152,6 +152,29 @@ def test_forward_is_bitwise_deterministic(causal, d):
         assert torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("algo", ["split_kv", "fa1_order"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_other_forwards_are_bitwise_deterministic(algo, causal, d):
+    # split-KV merges its slices in a fixed order and FA-1 order owns each
+    # head in one workgroup: neither uses atomics, so repeated runs on a grid
+    # that fills the GPU must agree to the bit
+    B, H, N = 2, 16, 2048 if algo == "split_kv" else 1024
+    x = _dev(make_inputs(B, H, N, d, seed=17))
+    if algo == "split_kv":
+        run = lambda: binding.attention_forward_split_kv(x["q"], x["k"], x["v"], causal,
+                                                         d ** -0.5, 4)
+    else:
+        run = lambda: binding.attention_forward_fa1_order(x["q"], x["k"], x["v"], causal,
+                                                          d ** -0.5)
+    o1, l1 = run()
+    for _ in range(3):
+        o2, l2 = run()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        assert torch.equal(l1, l2)
+
+
 def sample_rows(B, H, N, n_random=48, seed=0):
     rng = np.random.default_rng(seed)
     edge = {0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, N // 2,
