@@ -278,10 +278,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
       }
     }
     if constexpr (D == 128) {
-      // eight LDS reads ahead, then one MFMA per two V^T reads (interleaved
-      // A/B on MI355X, causal d = 128: +1.4 to +2.5 % with 8 waves, +3.5 to
-      // +3.9 % with 4; mixed at d = 64)
-      constexpr int kM = (BC / 16) * (D / 32), kAhead = 8;
+      // four LDS reads ahead, then one MFMA per two V^T reads (interleaved
+      // A/B on MI355X, causal d = 128: +1.7 to +3.5 % with 8 waves, +3.5 to
+      // +3.9 % with 4, against none; mixed at d = 64)
+      constexpr int kM = (BC / 16) * (D / 32), kAhead = 4;
       __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
       for (int i = 0; i < (2 * kM - kAhead) / 2; ++i) {
@@ -571,10 +571,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
     if constexpr (W == 8) {
       // Schedule of the block this lands in (in a pipelined step: the S
       // products of the next tile, P of this one and these PV products):
-      // eight LDS reads, then one MFMA per two reads, so the V^T reads are
-      // issued under the S MFMAs instead of just before their own MFMAs
-      // (the 4-wave variant measured 13 % slower with it)
-      constexpr int kM = (BC / 16) * (D / 32), kAhead = 8;
+      // four LDS reads, then one MFMA per two reads, so the V^T reads are
+      // issued under the S MFMAs instead of just before their own MFMAs.
+      // Depths 2 / 3 / 4 / 8 / 12 measured within 1 % of each other up to 8
+      // (4 best), 12 was 2.5 % slower; the 4-wave variant was 13 % slower
+      // with the schedule at all
+      constexpr int kM = (BC / 16) * (D / 32), kAhead = 4;
       __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
       for (int i = 0; i < (2 * kM - kAhead) / 2; ++i) {
