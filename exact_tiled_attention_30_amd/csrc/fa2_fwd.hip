@@ -278,9 +278,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
       }
     }
     if constexpr (D == 128) {
-      // four LDS reads ahead, then one MFMA per two V^T reads (interleaved
-      // A/B on MI355X, causal d = 128: +1.7 to +3.5 % with 8 waves, +3.5 to
-      // +3.9 % with 4, against none; mixed at d = 64)
+      // four LDS reads ahead, then one MFMA per two V^T reads (causal d = 128
+      // on MI355X: about +2 to +4 % against no such schedule; at d = 64 every
+      // depth tried measured within noise, so it is not used there)
       constexpr int kM = (BC / 16) * (D / 32), kAhead = 4;
       __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
@@ -573,9 +573,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
       // products of the next tile, P of this one and these PV products):
       // four LDS reads, then one MFMA per two reads, so the V^T reads are
       // issued under the S MFMAs instead of just before their own MFMAs.
-      // Depths 2 / 3 / 4 / 8 / 12 measured within 1 % of each other up to 8
-      // (4 best), 12 was 2.5 % slower; the 4-wave variant was 13 % slower
-      // with the schedule at all
+      // Depth 4 measured best of 2, 3, 4, 6, 8 and 12 (8: 1-2 % slower, 12:
+      // about 4 % slower); the 4-wave variant was 13 % slower with the
+      // schedule at all
       constexpr int kM = (BC / 16) * (D / 32), kAhead = 4;
       __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
