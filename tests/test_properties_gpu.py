@@ -8,6 +8,11 @@ at the full workload sizes (every element, no oracle run needed):
     and L_i = scale * q_i.k + ln(n_visible).
   * Backward: rows of dS sum to 0, so sum_j dK_j = 0; rows of P sum to 1, so
     sum_j dV_j = sum_i dO_i.
+  * Causal row 0 sees only key 0 (O_0 = V_0 exactly); the causal last row
+    sees every key (it equals the non-causal one); causal rows below M do not
+    depend on the tokens at or past M (prefix consistency); without a mask,
+    permuting the keys and values together changes nothing.  These compare
+    two GPU results, each within rounding of the exact value.
 
 Expected values are computed in fp64 on the host from the same bf16 inputs;
 the forward comparison uses the forward tolerance (oracle/compare.py).
@@ -84,3 +89,59 @@ def test_gradient_sums_at_full_size(atomic_dq):
     assert sk.max().item() <= 1e-2
     assert sv.max().item() <= 1e-2
     assert np.isfinite(dq.float().cpu().numpy()).all()
+
+
+def _close(a, b, what):
+    """Two GPU results of the same rows: each is within rounding of the exact
+    value, so they agree to the forward tolerance (1e-2 absolute plus a bf16
+    ulp for large values)."""
+    a, b = a.double(), b.double()
+    tol = 1e-2 + 2.0 ** -7 * b.abs()
+    bad = ((a - b).abs() > tol).sum().item()
+    assert bad == 0, (what, bad, (a - b).abs().max().item())
+
+
+@pytest.mark.parametrize("shape", SHAPES[:2], ids=IDS[:2])
+def test_causal_first_and_last_rows(shape):
+    # row 0 sees only key 0: O_0 = V_0 exactly, L_0 = scale * q_0.k_0; the
+    # last row sees every key: it equals the non-causal last row
+    B, H, N, d = shape
+    scale = d ** -0.5
+    x = {n: t.cuda() for n, t in make_inputs(B, H, N, d, seed=43).items()}
+    oc, lc = binding.attention_forward(x["q"], x["k"], x["v"], True, scale)
+    of, lf = binding.attention_forward(x["q"], x["k"], x["v"], False, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(oc[:, 0], x["v"][:, 0])
+    l0 = scale * (x["q"][:, 0].double() * x["k"][:, 0].double()).sum(-1)   # [B, H]
+    assert (lc[:, :, 0].double() - l0).abs().max().item() < 1e-4
+    _close(oc[:, -1], of[:, -1], "last row O")
+    assert (lc[:, :, -1] - lf[:, :, -1]).abs().max().item() < 1e-3
+
+
+@pytest.mark.parametrize("shape", SHAPES[:2], ids=IDS[:2])
+def test_causal_prefix_consistency(shape):
+    # causal rows i < M at length N see exactly the keys they see at length M
+    B, H, N, d = shape
+    M = N // 2 - 37
+    scale = d ** -0.5
+    x = {n: t.cuda() for n, t in make_inputs(B, H, N, d, seed=47).items()}
+    o_n, l_n = binding.attention_forward(x["q"], x["k"], x["v"], True, scale)
+    xm = {n: t[:, :M].contiguous() for n, t in x.items()}
+    o_m, l_m = binding.attention_forward(xm["q"], xm["k"], xm["v"], True, scale)
+    torch.cuda.synchronize()
+    _close(o_n[:, :M], o_m, "prefix O")
+    assert (l_n[:, :, :M] - l_m).abs().max().item() < 1e-3
+
+
+@pytest.mark.parametrize("shape", SHAPES[:2], ids=IDS[:2])
+def test_joint_key_value_permutation_leaves_full_attention_unchanged(shape):
+    B, H, N, d = shape
+    scale = d ** -0.5
+    x = {n: t.cuda() for n, t in make_inputs(B, H, N, d, seed=53).items()}
+    perm = torch.randperm(N, generator=torch.Generator().manual_seed(5)).cuda()
+    o1, l1 = binding.attention_forward(x["q"], x["k"], x["v"], False, scale)
+    o2, l2 = binding.attention_forward(x["q"], x["k"][:, perm].contiguous(),
+                                       x["v"][:, perm].contiguous(), False, scale)
+    torch.cuda.synchronize()
+    _close(o2, o1, "permuted O")
+    assert (l1 - l2).abs().max().item() < 1e-3
