@@ -135,6 +135,36 @@ def test_side_stream_and_determinism():
     assert rep["ok"], rep
 
 
+def test_concurrent_calls_on_two_streams():
+    # the library keeps no per-call state, so forward and backward calls
+    # running at once on two streams (different problems, interleaved
+    # launches) give the same bits as the same calls run one after the other
+    d = 128
+    xa = _dev(make_inputs(2, 8, 1500, d, seed=61, with_dout=True))
+    xb = _dev(make_inputs(1, 16, 2048, d, seed=62, with_dout=True))
+
+    def run(x, causal):
+        o, lse = binding.attention_forward(x["q"], x["k"], x["v"], causal, d ** -0.5)
+        g = binding.attention_backward(x["q"], x["k"], x["v"], o, lse, x["dout"], causal,
+                                       d ** -0.5)
+        return (o, lse) + tuple(g)
+
+    ref_a, ref_b = run(xa, True), run(xb, False)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    got_a, got_b = [], []
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            got_a.append(run(xa, True))
+        with torch.cuda.stream(sb):
+            got_b.append(run(xb, False))
+    torch.cuda.synchronize()
+    for ga in got_a:
+        assert all(torch.equal(u, w) for u, w in zip(ga, ref_a))
+    for gb in got_b:
+        assert all(torch.equal(u, w) for u, w in zip(gb, ref_b))
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_forward_is_bitwise_deterministic(causal, d):
