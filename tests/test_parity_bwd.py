@@ -62,6 +62,8 @@ SMALL = [
     (1, 1, 1, 128),      # a single token
     (1, 1, 130, 128),    # two key tiles, the second two keys long
     (2, 2, 600, 128),    # odd key-tile count: the middle causal tile runs alone
+    (3, 2, 129, 64),     # one row past a 128-key tile
+    (1, 1, 1000, 128),   # eight key tiles, the last one ragged
 ]
 
 
