@@ -4,11 +4,18 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
 One step is one pass of the hot path over one batch of resident, seeded
-synthetic inputs.  The default workload is B=8, H=16, N=1024, d=64 run both
-ways: a step is the non-causal forward followed by the causal forward on the
-same Q, K, V.  Other workloads (exact_tiled_attention_30_amd.inputs.WORKLOADS)
-can be named with --workload; a backward workload's step is one fa2_bwd call
-on O and L produced by fa2_fwd beforehand.
+synthetic inputs.  The default workload is the largest single-GPU one: the
+long-context causal forward B=1, H=16, N=32768, d=128 with 1 % of the key rows
+scaled by 8 (peaked softmax rows); a step is one fa2_fwd call.  Other
+workloads (exact_tiled_attention_30_amd.inputs.WORKLOADS) can be named with
+--workload, or the pair "fwd_b8_h16_n1024_d64_full+fwd_b8_h16_n1024_d64_causal"
+(both masks on the same inputs); a backward workload's step is one fa2_bwd
+call on O and L produced by fa2_fwd beforehand.
+
+Before the W warm-up steps the step runs back to back for at least
+--clock-warmup-ms of GPU time (reported as "clock_warmup_ms"): the GPU's clock
+takes tens of milliseconds to settle, and a kernel timed before that reads
+15-20 % slow.
 
 FLOPs follow the usual convention: 4*B*H*N^2*d per forward, halved if causal;
 a backward pass counts 2.5x its forward.  Timing uses HIP events on the stream
@@ -24,7 +31,11 @@ Prints ONE JSON line.  Besides the throughput it carries:
                 its HBM traffic from the committed rocprofv3 counter summary
                 (null when the kernel source changed since);
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample of
-                rows of the same workload, scaled to TFLOP/s.
+                the same workload (rows of a forward, whole heads of a
+                backward), scaled to TFLOP/s;
+  parity        the timed kernel's own outputs on that sample against the
+                oracle's (oracle/compare.py), with the bare max |dO| <= 1e-2
+                verdict beside the ulp-aware one.
 """
 from __future__ import annotations
 
@@ -41,7 +52,7 @@ if ROOT not in sys.path:
 
 METRIC = "fwd attention TFLOP/s (4BHN²d, ½ if causal) and % of MI355X bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz (dense)
-DEFAULT_PAIR = ("fwd_b8_h16_n1024_d64_full", "fwd_b8_h16_n1024_d64_causal")
+DEFAULT_WORKLOAD = "fwd_b1_h16_n32768_d128_causal_peaked"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -78,12 +89,14 @@ def load_traffic(kernel_key: str, backward: bool):
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     p.add_argument("--gpus", type=int, default=1)
-    # The warm-up is long enough (tens of ms of GPU work at the default
-    # workload) for the GPU clock to settle before the timed region.
-    p.add_argument("--steps", type=int, default=500)
-    p.add_argument("--warmup", type=int, default=300)
-    p.add_argument("--workload", default=None,
-                   help="one workload name (default: the N=1024 d=64 pair)")
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--clock-warmup-ms", type=float, default=300.0,
+                   help="GPU time the step runs back to back before the warm-up steps, "
+                        "so the clock has settled when timing starts")
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                   help="a workload name, or two forward workloads on the same inputs "
+                        "joined by '+'")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--algo", choices=("fa2", "split-kv", "fa1-order"), default="fa2",
                    help="forward workloads: fa2_fwd, fa2_fwd_split_kv (library's slice "
@@ -221,7 +234,7 @@ def main():
     from exact_tiled_attention_30_amd import binding
     from exact_tiled_attention_30_amd.inputs import WORKLOADS, inputs_for
 
-    names = DEFAULT_PAIR if args.workload is None else (args.workload,)
+    names = tuple(args.workload.split("+"))
     ws = [WORKLOADS[n] for n in names]
     base = ws[0]
     for w in ws[1:]:
@@ -285,6 +298,17 @@ def main():
                      w.scale)
             launches.append((w.name, bwd, w.flops()))
 
+    # clock warm-up: whole steps back to back until enough GPU time has passed
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    clock_warm_steps = 0
+    while (time.perf_counter() - w0) * 1e3 < args.clock_warmup_ms:
+        for _ in range(4):
+            for _, fn, _ in launches:
+                fn()
+        clock_warm_steps += 4
+        torch.cuda.synchronize()
+    clock_warm_ms = (time.perf_counter() - w0) * 1e3
     for _ in range(args.warmup):
         for _, fn, _ in launches:
             fn()
@@ -335,7 +359,12 @@ def main():
         "frac_of_measured": round(achieved / peak_clock, 4),
     }
 
-    cpu = None if args.no_cpu else cpu_baseline(ws, host, args.cpu_seconds)
+    if args.no_cpu:
+        cpu = parity = None
+    elif ws[0].backward:
+        cpu, parity = cpu_baseline_backward(ws[0], host, (dq, dk, dv))
+    else:
+        cpu, parity = cpu_baseline(ws, host, args.cpu_seconds, o, lse)
 
     line = {
         "metric": METRIC,
@@ -344,6 +373,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "clock_warmup_ms": round(clock_warm_ms, 1),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -367,23 +397,26 @@ def main():
                        for (n, _, f), t in zip(launches, per_kernel_ms)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(ws, host, target_s):
-    """Time the fp64 oracle on a bounded sample of rows of the same workload.
+def cpu_baseline(ws, host, target_s, o_gpu, lse_gpu):
+    """Time the fp64 oracle on a bounded sample of rows of the same workload,
+    and compare the GPU's outputs on those rows with it.
 
     Rows are independent, so the FLOPs of a sample are exact: 4*n_vis*d per
     row (n_vis visible keys).  Inputs are widened to fp64 once, outside the
-    timed calls; the sample size comes from a short calibration run.
+    timed calls; the sample size comes from a short calibration run.  o_gpu /
+    lse_gpu hold the outputs of the step's last launch, which is compared.
     """
     import numpy as np
+    import torch
 
     import oracle
+    from oracle.compare import forward_report
 
-    if any(w.backward for w in ws):
-        return None
     n_thr = oracle.num_threads()
     rng = np.random.default_rng(0)
     q64, k64, v64 = (oracle.widen(host[n]) for n in ("q", "k", "v"))
@@ -398,33 +431,75 @@ def cpu_baseline(ws, host, target_s):
 
     def timed(w, rows):
         t0 = time.perf_counter()
-        oracle.attention_forward_rows(q64, k64, v64, w.causal, w.scale, rows)
-        return time.perf_counter() - t0
+        ref = oracle.attention_forward_rows(q64, k64, v64, w.causal, w.scale, rows)
+        return time.perf_counter() - t0, ref
 
     calib = max(32, 4 * n_thr)
     cal_f = cal_t = 0.0
     for w in ws:
         rows = rows_for(w, calib)
-        cal_t += timed(w, rows)
+        cal_t += timed(w, rows)[0]
         cal_f += flops(w, rows)
     rate = cal_f / max(cal_t, 1e-9)
 
     total_f = total_t = 0.0
     desc = []
-    for w in ws:
+    parity = None
+    for j, w in enumerate(ws):
         per_row = 4.0 * (w.N / 2 if w.causal else w.N) * w.d
         n = int(min(w.B * w.H * w.N, max(calib, target_s / len(ws) * rate / per_row)))
         rows = rows_for(w, n)
-        total_t += timed(w, rows)
+        t, (o_ref, lse_ref) = timed(w, rows)
+        total_t += t
         total_f += flops(w, rows)
         desc.append(f"{n} random rows of {w.name}")
+        if j == len(ws) - 1:
+            b, h, i = (torch.as_tensor(rows[:, c], device=o_gpu.device) for c in range(3))
+            rep = forward_report(o_gpu[b, i, h].cpu(), lse_gpu[b, h, i].cpu(), o_ref, lse_ref)
+            parity = {"workload": w.name, "rows": n, **rep}
     return {
         "value": round(total_f / total_t / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": n_thr,
         "kind": "oracle",
         "sample": "; ".join(desc) + f"; fp64, {total_t:.1f} s of oracle compute",
-    }
+    }, parity
+
+
+def cpu_baseline_backward(w, host, grads_gpu):
+    """Time the fp64 oracle's backward on whole heads of the workload (one
+    head per OpenMP thread, so every core works), and compare the GPU's
+    gradients of those heads with it.  FLOPs by the same convention as the
+    GPU: 2.5x the forward's 4*N^2*d per head, halved if causal."""
+    import numpy as np
+
+    import oracle
+    from oracle.compare import gradient_report
+
+    n_thr = oracle.num_threads()
+    rng = np.random.default_rng(0)
+    n_heads = min(w.B * w.H, n_thr)
+    pick = rng.choice(w.B * w.H, size=n_heads, replace=False)
+    heads = sorted((int(x) // w.H, int(x) % w.H) for x in pick)
+    widened = [oracle.widen(host[n]) for n in ("q", "k", "v", "dout")]
+    t0 = time.perf_counter()
+    ref = oracle.attention_backward(*widened, w.causal, w.scale, heads)
+    t = time.perf_counter() - t0
+    per_head = 2.5 * 4.0 * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    parity = {"workload": w.name, "heads": len(heads)}
+    for name, g in zip(("dq", "dk", "dv"), grads_gpu):
+        got = np.stack([g[b, :, h, :].double().cpu().numpy() for (b, h) in heads])
+        rep = gradient_report(got, ref[name])
+        parity[name] = {k: rep[k] for k in ("max_rel", "mean_rel", "ok")}
+    parity["ok"] = all(parity[n]["ok"] for n in ("dq", "dk", "dv"))
+    return {
+        "value": round(per_head * len(heads) / t / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": n_thr,
+        "kind": "oracle",
+        "sample": f"{len(heads)} whole heads (b, h) of {w.name}, forward recomputed and "
+                  f"backward; fp64, {t:.1f} s of oracle compute",
+    }, parity
 
 
 if __name__ == "__main__":

@@ -8,7 +8,7 @@ library is missing the call fails loudly.
 Names mirror include/fa2.h: fa2_fwd, fa2_bwd, fa2_bwd_workspace_bytes,
 fa2_bwd_atomic_dq, fa2_bwd_atomic_dq_workspace_bytes, fa2_fwd_split_kv,
 fa2_fwd_split_kv_workspace_bytes, fa2_fwd_fa1_order, fa2_fwd_fa1_order_workspace_bytes,
-fa2_status_string.
+fa2_fwd_variant, fa2_bwd_variant, fa2_variant_name, fa2_calibrate_mfma, fa2_status_string.
 """
 from __future__ import annotations
 
@@ -66,6 +66,12 @@ def lib():
     L.fa2_fwd_fa1_order.restype = _i
     L.fa2_calibrate_mfma.argtypes = [_vp, _i, _i, _vp]
     L.fa2_calibrate_mfma.restype = _i
+    L.fa2_fwd_variant.argtypes = [_i, _i, _i, _i, _i, _i]
+    L.fa2_fwd_variant.restype = _i
+    L.fa2_bwd_variant.argtypes = [_i, _i, _i, _i, _i]
+    L.fa2_bwd_variant.restype = _i
+    L.fa2_variant_name.argtypes = [_i]
+    L.fa2_variant_name.restype = ctypes.c_char_p
     L.fa2_status_string.argtypes = [_i]
     L.fa2_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -74,6 +80,21 @@ def lib():
 
 def fa2_status_string(status: int) -> str:
     return lib().fa2_status_string(int(status)).decode()
+
+
+def fa2_fwd_variant(B: int, H: int, N: int, d: int, causal: bool, resident_wgs: int = 0) -> int:
+    """Id of the kernel configuration fa2_fwd launches (-1: invalid or empty);
+    resident_wgs <= 0 asks the current device (see include/fa2.h)."""
+    return int(lib().fa2_fwd_variant(B, H, N, d, int(bool(causal)), int(resident_wgs)))
+
+
+def fa2_bwd_variant(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    """Id of the kernel configuration fa2_bwd launches (-1: invalid or empty)."""
+    return int(lib().fa2_bwd_variant(B, H, N, d, int(bool(causal))))
+
+
+def fa2_variant_name(variant: int) -> str:
+    return lib().fa2_variant_name(int(variant)).decode()
 
 
 def fa2_calibrate_mfma(out, blocks: int, iters: int, stream=None) -> None:
@@ -124,20 +145,33 @@ def _require(t, dtype, name):
     del torch
 
 
+def _shapes(named, lse, B, N, H, d):
+    """Shapes first (they need no device): every [B, N, H, d] tensor, then lse
+    [B, H, N] -- the kernels read B*H*N floats of it in that layout."""
+    for t, name in named:
+        if tuple(t.shape) != (B, N, H, d):
+            raise ValueError(f"{name} must have shape {(B, N, H, d)}")
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"lse must have shape {(B, H, N)}")
+
+
+def _fwd_checks(q, k, v, o, lse):
+    import torch
+
+    B, N, H, d = _bnhd(q)
+    named = ((q, "q"), (k, "k"), (v, "v"), (o, "o"))
+    _shapes(named, lse, B, N, H, d)
+    for t, name in named:
+        _require(t, torch.bfloat16, name)
+    _require(lse, torch.float32, "lse")
+    return B, N, H, d
+
+
 def fa2_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
     """Enqueue the forward pass on `stream` (default: torch's current stream).
 
     q, k, v, o: bf16 [B, N, H, d]; lse: fp32 [B, H, N].  Raises Fa2Error."""
-    import torch
-
-    B, N, H, d = _bnhd(q)
-    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
-        _require(t, torch.bfloat16, name)
-        if tuple(t.shape) != (B, N, H, d):
-            raise ValueError(f"{name} must have shape {(B, N, H, d)}")
-    _require(lse, torch.float32, "lse")
-    if tuple(lse.shape) != (B, H, N):
-        raise ValueError(f"lse must have shape {(B, H, N)}")
+    B, N, H, d = _fwd_checks(q, k, v, o, lse)
     _check(lib().fa2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                          int(bool(causal)), float(scale), _stream(q, stream)))
 
@@ -154,14 +188,7 @@ def fa2_fwd_split_kv(q, k, v, o, lse, workspace, causal: bool, scale: float, n_s
     at least fa2_fwd_split_kv_workspace_bytes(..., n_split) bytes.  Raises Fa2Error."""
     import torch
 
-    B, N, H, d = _bnhd(q)
-    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
-        _require(t, torch.bfloat16, name)
-        if tuple(t.shape) != (B, N, H, d):
-            raise ValueError(f"{name} must have shape {(B, N, H, d)}")
-    _require(lse, torch.float32, "lse")
-    if tuple(lse.shape) != (B, H, N):
-        raise ValueError(f"lse must have shape {(B, H, N)}")
+    B, N, H, d = _fwd_checks(q, k, v, o, lse)
     _require(workspace, torch.uint8, "workspace")
     _check(lib().fa2_fwd_split_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
                                   workspace.numel(), B, H, N, d, int(bool(causal)), float(scale),
@@ -179,14 +206,7 @@ def fa2_fwd_fa1_order(q, k, v, o, lse, workspace, causal: bool, scale: float,
     fa2_fwd_fa1_order_workspace_bytes(...) bytes.  Raises Fa2Error."""
     import torch
 
-    B, N, H, d = _bnhd(q)
-    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
-        _require(t, torch.bfloat16, name)
-        if tuple(t.shape) != (B, N, H, d):
-            raise ValueError(f"{name} must have shape {(B, N, H, d)}")
-    _require(lse, torch.float32, "lse")
-    if tuple(lse.shape) != (B, H, N):
-        raise ValueError(f"lse must have shape {(B, H, N)}")
+    B, N, H, d = _fwd_checks(q, k, v, o, lse)
     _require(workspace, torch.uint8, "workspace")
     _check(lib().fa2_fwd_fa1_order(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
                                    workspace.numel(), B, H, N, d, int(bool(causal)), float(scale),
@@ -205,11 +225,11 @@ def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, scale, strea
     import torch
 
     B, N, H, d = _bnhd(q)
-    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"),
-                    (dk, "dk"), (dv, "dv")):
+    named = ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+             (dv, "dv"))
+    _shapes(named, lse, B, N, H, d)
+    for t, name in named:
         _require(t, torch.bfloat16, name)
-        if tuple(t.shape) != (B, N, H, d):
-            raise ValueError(f"{name} must have shape {(B, N, H, d)}")
     _require(lse, torch.float32, "lse")
     _require(workspace, torch.uint8, "workspace")
     return (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),

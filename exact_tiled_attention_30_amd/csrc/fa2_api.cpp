@@ -247,6 +247,25 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
                     causal, scale, stream, false);
 }
 
+int fa2_fwd_variant(int B, int H, int N, int d, int causal, int resident_wgs) {
+  size_t elems = 0, rows = 0;
+  if (check_shape(B, H, N, d, 1.0f, &elems, &rows) != FA2_OK || elems == 0) return -1;
+  if (resident_wgs <= 0 && causal && d == 128) resident_wgs = fa2::fwd_resident_d128();
+  return fa2::fwd_variant(B, H, N, d, causal != 0, resident_wgs);
+}
+
+int fa2_bwd_variant(int B, int H, int N, int d, int causal) {
+  size_t elems = 0, rows = 0;
+  if (check_shape(B, H, N, d, 1.0f, &elems, &rows) != FA2_OK || elems == 0) return -1;
+  return fa2::bwd_variant(B, H, N, d, causal != 0);
+}
+
+const char* fa2_variant_name(int variant) {
+  const char* n = fa2::fwd_variant_name(variant);
+  if (!n) n = fa2::bwd_variant_name(variant);
+  return n ? n : "";
+}
+
 int fa2_calibrate_mfma(float* out, int blocks, int iters, void* stream) {
   if (out == nullptr) return FA2_ERR_NULLPTR;
   if (blocks < 1 || iters < 1) return FA2_ERR_SHAPE;

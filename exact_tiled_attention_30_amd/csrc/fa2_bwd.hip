@@ -93,15 +93,17 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
 }
 
 // ---------------------------------------------------------------- B2 ----
-// dq = bf16(dq_acc), 8 elements per thread.
+// dq = bf16(scale * dq_acc), 8 elements per thread.  The accumulator holds
+// the unscaled sum of dS K, so the atomic adds work on O(1) values even when
+// scale is tiny (a subnormal dQ is formed once, here, not summed).
 __global__ __launch_bounds__(256) void bwd_convert_dq_kernel(const float* __restrict__ dq_acc,
                                                              uint16_t* __restrict__ dq,
-                                                             long long n8) {
+                                                             long long n8, float scale) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
   const f32x4 a = *(const f32x4*)(dq_acc + 8 * i);
   const f32x4 b = *(const f32x4*)(dq_acc + 8 * i + 4);
-  const bf16x8 r = to_bf16x8(f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+  const bf16x8 r = to_bf16x8(f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]} * scale);
   *(u32x4*)(dq + 8 * i) = as_u32x4(r);
 }
 
@@ -449,7 +451,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
     wait_dma_and_lds();
     __syncthreads();
 
-    // dQ partial = scale * dS K over this workgroup's 128 keys.  Its atomic
+    // dQ partial = dS K over this workgroup's 128 keys (scale is applied
+    // when the accumulator is rounded to bf16).  Its atomic
     // adds are issued at the start of the next step (flush_dq), so their
     // round trips overlap that step's work instead of the wait below.
 #pragma unroll
@@ -464,7 +467,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
         acc = mfma32(a, bk, acc);
       }
       interleave_lds_mfma<kBwdKeys / 16, 4, 2>();
-      dq_pend[u] = acc * scale;
+      dq_pend[u] = acc;
     }
     q0_pend = q0;
     }
@@ -1055,7 +1058,7 @@ hipError_t launch_bwd_atomic(const BwdParams& p) {
   launch_kv_outer<D, CAUSAL, true>(p);
   const long long n8 = (long long)p.B * p.N * p.H * D / 8;
   hipLaunchKernelGGL(bwd_convert_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
-                     p.stream, p.dq_acc, (uint16_t*)p.dq, n8);
+                     p.stream, p.dq_acc, (uint16_t*)p.dq, n8, p.scale);
   return hipGetLastError();
 }
 
@@ -1065,10 +1068,7 @@ hipError_t launch_bwd_atomic(const BwdParams& p) {
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_two_pass(const BwdParams& p) {
   (void)hipGetLastError();
-  constexpr int kCus = 256;
-  const long long items8 =
-      (long long)p.B * p.H * (CAUSAL ? ((p.N + 255) / 256 + 1) / 2 : (p.N + 255) / 256);
-  if (items8 < 2 * kCus) launch_dq_pass<D, 4, CAUSAL>(p);
+  if (bwd_dq_waves(p.B, p.H, p.N, p.causal) == 4) launch_dq_pass<D, 4, CAUSAL>(p);
   else launch_dq_pass<D, 8, CAUSAL>(p);
   // d = 128: the 8-wave pass (two waves per SIMD); d = 64 fits two 4-wave
   // workgroups per CU already, where the 4-wave pass measures faster
@@ -1078,6 +1078,33 @@ hipError_t launch_bwd_two_pass(const BwdParams& p) {
 }
 
 }  // namespace
+
+// Waves per workgroup of the dQ pass: 8 (256-row Q tiles), or 4 when the
+// 8-wave grid would give fewer than two workgroups per CU.
+int bwd_dq_waves(int B, int H, int N, bool causal) {
+  constexpr long long kCus = 256;
+  const long long items8 =
+      (long long)B * H * (causal ? ((N + 255) / 256 + 1) / 2 : (N + 255) / 256);
+  return items8 < 2 * kCus ? 4 : 8;
+}
+
+int bwd_variant(int B, int H, int N, int d, bool causal) {
+  const int w8 = bwd_dq_waves(B, H, N, causal) == 8;
+  return kBwdFirst + ((d == 128) << 2) + ((int)causal << 1) + w8;
+}
+
+const char* bwd_variant_name(int v) {
+  static const char* const names[8] = {
+      "bwd_dq_kernel<64,4,false>+bwd_dl_kernel<64,false,false>",
+      "bwd_dq_kernel<64,8,false>+bwd_dl_kernel<64,false,false>",
+      "bwd_dq_kernel<64,4,true>+bwd_dl_kernel<64,true,false>",
+      "bwd_dq_kernel<64,8,true>+bwd_dl_kernel<64,true,false>",
+      "bwd_dq_kernel<128,4,false>+bwd_kv_pair_kernel<128,false>",
+      "bwd_dq_kernel<128,8,false>+bwd_kv_pair_kernel<128,false>",
+      "bwd_dq_kernel<128,4,true>+bwd_kv_pair_kernel<128,true>",
+      "bwd_dq_kernel<128,8,true>+bwd_kv_pair_kernel<128,true>"};
+  return v >= kBwdFirst && v < kBwdFirst + 8 ? names[v - kBwdFirst] : nullptr;
+}
 
 hipError_t launch_bwd(const BwdParams& p) {
   if (p.d == 64)

@@ -86,6 +86,23 @@ size_t bwd_delta_bytes(int B, int H, int N);
 size_t bwd_dq_acc_bytes(int B, int H, int N, int d);
 size_t fa1_ml_bytes(int B, int H, int N);
 
+// Kernel configurations the host dispatch picks from (diagnostic ids, also
+// exported through fa2_fwd_variant / fa2_bwd_variant).
+enum Variant {
+  kFwdD64Nc4 = 0, kFwdD64Nc8, kFwdD128Sp4, kFwdD128Sp8,
+  kFwdD64CausalDealt, kFwdD64CausalOne, kFwdD64CausalPair4, kFwdD64CausalPair8,
+  kFwdD128CausalDealt, kFwdD128CausalOne, kFwdD128CausalPair4, kFwdD128CausalPair8,
+  kFwdCount,
+  kBwdFirst = 16,  // 16 + 4*(d == 128) + 2*causal + (dQ pass has 8 waves)
+  kBwdCount = 8,
+};
+int fwd_variant(int B, int H, int N, int d, bool causal, int resident_d128);
+const char* fwd_variant_name(int v);
+int fwd_resident_d128();  // occupancy query of the d = 128 dealt causal kernel
+int bwd_dq_waves(int B, int H, int N, bool causal);
+int bwd_variant(int B, int H, int N, int d, bool causal);
+const char* bwd_variant_name(int v);
+
 hipError_t launch_fwd(const FwdParams& p);
 hipError_t launch_fwd_split_kv(const FwdParams& p);
 int split_kv_slices(int B, int H, int N, int requested);

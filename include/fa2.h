@@ -186,6 +186,29 @@ int fa2_fwd_fa1_order(const void* q, const void* k, const void* v, void* o, floa
  */
 int fa2_calibrate_mfma(float* out, int blocks, int iters, void* stream);
 
+/*
+ * Diagnostics, not part of the attention path: which kernel configuration
+ * (tile shape, waves per workgroup, causal work assignment) fa2_fwd and
+ * fa2_bwd launch for a problem, so tests can show that every configuration
+ * the dispatch can pick is exercised, and profiles can name the kernel they
+ * time.  Pure host arithmetic on the sizes, with no device work and no
+ * allocation.
+ *   fa2_fwd_variant: an id in [0, 12); resident_wgs is the number of
+ *     workgroups of the 4-wave d = 128 causal kernel one CU holds at once,
+ *     which decides whether a causal d = 128 grid is dealt to the CUs by
+ *     weight; resident_wgs <= 0 asks the current device (the occupancy query
+ *     fa2_fwd itself makes; 0 without a usable device).  Ignored unless
+ *     causal and d == 128.
+ *   fa2_bwd_variant: an id in [16, 24), the dQ pass and dK/dV pass fa2_bwd
+ *     launches.
+ * Both return -1 for arguments fa2_fwd / fa2_bwd would reject or an empty
+ * problem.  fa2_variant_name returns the kernel template(s) of an id as a
+ * static string, or "" for an unknown id.
+ */
+int fa2_fwd_variant(int B, int H, int N, int d, int causal, int resident_wgs);
+int fa2_bwd_variant(int B, int H, int N, int d, int causal);
+const char* fa2_variant_name(int variant);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa2_status_string(int status);
 

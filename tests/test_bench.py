@@ -7,6 +7,7 @@ import subprocess
 import sys
 
 import pytest
+import torch
 
 import bench
 from exact_tiled_attention_30_amd.inputs import WORKLOADS, Workload, inputs_for
@@ -46,14 +47,43 @@ def test_traffic_is_tied_to_the_kernel_sources(tmp_path, monkeypatch):
 
 
 def test_cpu_baseline_record():
+    # the parity leg is plumbing here: the "GPU" outputs are the oracle's own,
+    # rounded to bf16 as the library's are, so they must pass
+    import oracle
+
     w = WORKLOADS["fwd_b1_h1_n128_d64_full"]
     wc = Workload("fwd_b1_h1_n128_d64_causal", 1, 1, 128, 64, True)
-    rec = bench.cpu_baseline([w, wc], inputs_for(w), 0.05)
+    x = inputs_for(w)
+    o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], True, wc.scale)
+    o = torch.from_numpy(o_ref).to(torch.bfloat16)
+    lse = torch.from_numpy(lse_ref).float()
+    rec, parity = bench.cpu_baseline([w, wc], x, 0.05, o, lse)
     assert set(rec) == {"value", "unit", "cores", "kind", "sample"}
     assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
     assert rec["value"] > 0 and rec["cores"] >= 1
     # the whole workload is small: every row is in the sample
     assert rec["sample"].startswith("128 random rows of fwd_b1_h1_n128_d64_full")
+    assert parity["workload"] == wc.name and parity["ok"] and parity["rows"] == 128
+    assert "max_abs_dO_le_1e-2" in parity
+    # and a wrong output is reported as such
+    rec, parity = bench.cpu_baseline([wc], x, 0.05, o * 1.1, lse)
+    assert not parity["ok"]
+
+
+def test_cpu_baseline_backward_record():
+    import oracle
+
+    w = Workload("bwd_b1_h3_n200_d64_causal", 1, 3, 200, 64, True, backward=True)
+    x = inputs_for(w)
+    ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["dout"], True, w.scale)
+    grads = [torch.from_numpy(ref[n]).reshape(1, 3, 200, 64).permute(0, 2, 1, 3)
+             .contiguous().to(torch.bfloat16) for n in ("dq", "dk", "dv")]
+    rec, parity = bench.cpu_baseline_backward(w, x, grads)
+    assert rec["kind"] == "oracle" and rec["value"] > 0 and rec["cores"] >= 1
+    assert "whole heads" in rec["sample"]
+    assert parity["ok"] and parity["heads"] == min(3, rec["cores"])
+    rec, parity = bench.cpu_baseline_backward(w, x, [grads[0], grads[1] * 1.2, grads[2]])
+    assert not parity["ok"] and not parity["dk"]["ok"]
 
 
 @pytest.mark.gpu
@@ -67,11 +97,14 @@ def test_bench_json_line():
     d = json.loads(lines[0])
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
-                "roofline", "cpu_baseline"):
+                "roofline", "cpu_baseline", "parity", "clock_warmup_ms"):
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 2
     assert d["unit"] == "TFLOP/s" and d["higher_is_better"] is True and d["dtype"] == "bf16"
-    assert d["config"]["workload"] == "fwd_b8_h16_n1024_d64_full+fwd_b8_h16_n1024_d64_causal"
+    # the largest single-GPU workload is the default
+    assert d["config"]["workload"] == "fwd_b1_h16_n32768_d128_causal_peaked"
+    assert d["clock_warmup_ms"] >= 300
+    assert d["parity"]["ok"] and d["parity"]["rows"] > 0
     assert d["value"] > 0
     rf = d["roofline"]
     assert rf["bound"] == "mfma" and rf["peak"] == 2516.6 and rf["unit"] == "TFLOP/s"

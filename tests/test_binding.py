@@ -13,6 +13,12 @@ def bf16(*shape):
     return torch.zeros(shape, dtype=torch.bfloat16)
 
 
+def strided(t):
+    """A non-contiguous view of the same shape and dtype."""
+    wide = torch.zeros(t.shape[:-1] + (2 * t.shape[-1],), dtype=t.dtype)
+    return wide[..., ::2]
+
+
 def fwd_args():
     q, k, v, o = (bf16(B, N, H, D) for _ in range(4))
     lse = torch.zeros((B, H, N), dtype=torch.float32)
@@ -27,7 +33,7 @@ def test_forward_rejects_bad_tensors():
         # the bf16 tensors fail first on the host check, so give lse alone a bad dtype
         binding._require(lse.double(), torch.float32, "lse")
     with pytest.raises(ValueError, match="contiguous"):
-        binding.fa2_fwd(q.transpose(1, 2), k, v, o, lse, False, 0.125)
+        binding.fa2_fwd(strided(q), k, v, o, lse, False, 0.125)
     with pytest.raises(ValueError, match="device tensor"):
         binding.fa2_fwd(q, k, v, o, lse, False, 0.125)
     with pytest.raises(ValueError, match=r"\[B, N, H, d\]"):
@@ -45,11 +51,21 @@ def test_backward_rejects_bad_tensors():
         with pytest.raises(TypeError):
             f(q.half(), k, v, o, lse, do, dq, dk, dv, ws, True, 0.125)
         with pytest.raises(ValueError, match="contiguous"):
-            f(q.transpose(1, 2), k, v, o, lse, do, dq, dk, dv, ws, True, 0.125)
+            f(strided(q), k, v, o, lse, do, dq, dk, dv, ws, True, 0.125)
         with pytest.raises(ValueError, match="device tensor"):
             f(q, k, v, o, lse, do, dq, dk, dv, ws, True, 0.125)
     with pytest.raises(ValueError, match="device tensor"):
         binding.attention_backward(q, k, v, o, lse, do, True)
+    # lse: the kernels read B*H*N floats in [B, H, N] order, so a short lse or
+    # one in another layout ([B, N, H] here) is refused before any library call
+    for bad_lse in (torch.zeros((B, H, N - 1)), torch.zeros((B, N, H)), torch.zeros(B * H * N)):
+        for f in (binding.fa2_bwd, binding.fa2_bwd_atomic_dq):
+            with pytest.raises(ValueError, match=r"lse must have shape"):
+                f(q, k, v, o, bad_lse, do, dq, dk, dv, ws, True, 0.125)
+        with pytest.raises(ValueError, match=r"lse must have shape"):
+            binding.fa2_fwd(q, k, v, o, bad_lse, False, 0.125)
+    with pytest.raises(ValueError, match=r"dout must have shape"):
+        binding.fa2_bwd(q, k, v, o, lse, do[:, :-1], dq, dk, dv, ws, True, 0.125)
 
 
 def test_calibration_rejects_bad_output():

@@ -38,10 +38,11 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa2_bwd", "fa2_bwd_atomic_dq",
                                     "fa2_bwd_atomic_dq_workspace_bytes",
-                                    "fa2_bwd_workspace_bytes", "fa2_calibrate_mfma",
-                                    "fa2_fwd", "fa2_fwd_fa1_order",
+                                    "fa2_bwd_variant", "fa2_bwd_workspace_bytes",
+                                    "fa2_calibrate_mfma", "fa2_fwd", "fa2_fwd_fa1_order",
                                     "fa2_fwd_fa1_order_workspace_bytes", "fa2_fwd_split_kv",
-                                    "fa2_fwd_split_kv_workspace_bytes", "fa2_status_string"]
+                                    "fa2_fwd_split_kv_workspace_bytes", "fa2_fwd_variant",
+                                    "fa2_status_string", "fa2_variant_name"]
 
 
 def test_library_exports_every_declared_symbol(L):

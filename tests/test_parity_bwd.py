@@ -81,10 +81,13 @@ def test_small_shapes_every_element(shape, causal, atomic_dq):
     check(grads, ref, heads, f"{shape} causal={causal}")
 
 
+SCALE_SHAPE = (1, 2, 190)  # (B, H, N) of the unusual-scale cases (causal)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale", [-0.1, 0.3])
 def test_unusual_scales(scale, d):
-    B, H, N = 1, 2, 190
+    B, H, N = SCALE_SHAPE
     print(f"[bwd scale] scale={scale} d={d}", flush=True)
     x = make_inputs(B, H, N, d, seed=4, with_dout=True)
     grads = run_bwd(x, True, scale)
@@ -105,15 +108,83 @@ def test_gradient_sums_on_gpu():
     assert (((dv.sum(dim=1) - do.sum(dim=1)).abs()) <= 1e-2 * do.abs().sum(dim=1)).all()
 
 
+def spread_heads(B, H, n=16, seed=0):
+    """n distinct (b, h) heads (all of them if there are fewer): the first,
+    the last, and seeded picks in between."""
+    rng = np.random.default_rng(seed)
+    heads = {(0, 0), (B - 1, H - 1)}
+    while len(heads) < min(n, B * H):
+        heads.add((int(rng.integers(B)), int(rng.integers(H))))
+    return sorted(heads)
+
+
 @pytest.mark.parametrize("atomic_dq", STRATEGIES, ids=STRATEGY_IDS)
 def test_full_size_backward_workload_heads(atomic_dq):
+    # the full-size backward workload at its stated seed, 16 of its 64 heads
+    # compared element by element
     w = WORKLOADS["bwd_b4_h16_n4096_d128_causal"]
     print(f"[bwd full-size] {w.name} atomic_dq={atomic_dq}", flush=True)
     x = make_inputs(w.B, w.H, w.N, w.d, seed=w.seed, with_dout=True)
     grads = run_bwd(x, w.causal, w.scale, atomic_dq)
-    heads = [(0, 0), (3, 15), (1, 7), (2, 3)]
+    heads = spread_heads(w.B, w.H, 16, seed=1)
     ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["dout"], w.causal, w.scale, heads)
     check(grads, ref, heads, w.name)
+
+
+# Grids large enough for the 8-wave dQ pass, non-causal and at d = 64 (the
+# full-size workload covers causal d = 128): 16 whole heads each.
+DISPATCH_SHAPES = [(4, 16, 4096, 128, False), (8, 16, 2048, 64, False),
+                   (8, 16, 2048, 64, True)]
+
+
+@pytest.mark.parametrize("case", DISPATCH_SHAPES,
+                         ids=lambda c: "b{}h{}n{}d{}-{}".format(*c[:4], "causal" if c[4] else "full"))
+def test_eight_wave_dq_pass_shapes(case):
+    B, H, N, d, causal = case
+    v = binding.fa2_bwd_variant(B, H, N, d, causal)
+    print(f"[bwd dispatch] {case} variant={binding.fa2_variant_name(v)}", flush=True)
+    x = make_inputs(B, H, N, d, seed=31, with_dout=True)
+    grads = run_bwd(x, causal, d ** -0.5)
+    heads = spread_heads(B, H, 16, seed=2)
+    ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["dout"], causal, d ** -0.5, heads)
+    check(grads, ref, heads, str(case))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scale", [0.0, -1e-39, 1e-39])
+@pytest.mark.parametrize("atomic_dq", STRATEGIES, ids=STRATEGY_IDS)
+def test_zero_and_subnormal_scales(atomic_dq, scale, d):
+    # scale = 0: every score is 0, P is uniform over the visible keys, dV is
+    # the prefix mean of dO and dQ = dK = 0 exactly.  |scale| = 1e-39 is
+    # subnormal in fp32 (so is scale * log2 e): P is uniform to fp32
+    # precision and dQ, dK are scale times an O(1) sum, subnormal numbers
+    # that fp32 and bf16 still hold to a few significant bits
+    B, H, N = SCALE_SHAPE
+    print(f"[bwd scale] scale={scale} d={d} atomic_dq={atomic_dq}", flush=True)
+    x = make_inputs(B, H, N, d, seed=4, with_dout=True)
+    grads = run_bwd(x, True, scale, atomic_dq)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["dout"], True, scale, heads)
+    if scale == 0.0:
+        assert not grads[0].any() and not grads[1].any()
+    check(grads, ref, heads, f"scale={scale}")
+
+
+def bwd_parity_cases():
+    """(B, H, N, d, causal) of every fa2_bwd call the parity tests here
+    compare with the oracle."""
+    cases = [(*s, c) for s in SMALL for c in (False, True)]
+    cases += [(*SCALE_SHAPE, d, True) for d in (64, 128)]
+    w = WORKLOADS["bwd_b4_h16_n4096_d128_causal"]
+    cases.append((w.B, w.H, w.N, w.d, w.causal))
+    cases += DISPATCH_SHAPES
+    return cases
+
+
+def test_every_backward_configuration_is_compared():
+    seen = {binding.fa2_bwd_variant(*c) for c in bwd_parity_cases()}
+    missing = [binding.fa2_variant_name(v) for v in range(16, 24) if v not in seen]
+    assert not missing, missing
 
 
 @pytest.mark.parametrize("shape", [(2, 2, 300, 64), (1, 8, 2048, 128)],

@@ -57,6 +57,9 @@ SMALL_SHAPES = [
 ]
 
 
+SCALE_SHAPE = (1, 2, 300)  # (B, H, N) of the unusual-scale cases, both d and masks
+
+
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "b{}h{}n{}d{}".format(*s))
 def test_small_shapes_every_element(shape, causal):
@@ -78,7 +81,7 @@ def test_small_shapes_every_element(shape, causal):
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1.0 / 128, 1e-40, -1e-45, 1e-38, 20.0])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_unusual_scales(scale, causal, d):
-    B, H, N = 1, 2, 300
+    B, H, N = SCALE_SHAPE
     x = make_inputs(B, H, N, d, seed=5, peaked_fraction=0.02)
     print(f"[fwd scale] scale={scale} causal={causal} d={d}", flush=True)
     o, lse = run_fwd(x, causal, scale)
@@ -222,11 +225,47 @@ def sample_rows(B, H, N, n_random=48, seed=0):
     return np.array(rows, dtype=np.int64)
 
 
+def spread_rows(B, H, N, n_total=4096, seed=0):
+    """At least n_total distinct (b, h, i) rows covering every head alike:
+    per head the first and last rows, rows on each side of the 128- and
+    256-row Q tile edges nearest a random point, and random rows."""
+    rng = np.random.default_rng(seed)
+    per_head = max(8, -(-n_total // (B * H)))
+    rows = set()
+    for b in range(B):
+        for h in range(H):
+            pick = {0, N - 1}
+            t = int(rng.integers(N))
+            for edge in (t - t % 128, t - t % 256):
+                pick.update(i for i in (edge - 1, edge, edge + 1) if 0 <= i < N)
+            while len(pick) < min(per_head, N):
+                pick.add(int(rng.integers(N)))
+            rows.update((b, h, i) for i in pick)
+    out = np.array(sorted(rows), dtype=np.int64)
+    assert len(out) >= min(n_total, B * H * N)
+    return out
+
+
+def check_rows(o, lse, x, causal, scale, rows):
+    o_ref, lse_ref = oracle.attention_forward_rows(x["q"], x["k"], x["v"], causal, scale, rows)
+    b, h, i = (torch.as_tensor(rows[:, c], device="cuda") for c in range(3))
+    rep = forward_report(o[b, i, h].cpu(), lse[b, h, i].cpu(), o_ref, lse_ref)
+    print(f"  {len(rows)} rows: {rep}", flush=True)
+    assert rep["ok"], rep
+
+
 FWD_WORKLOADS = [w for w in WORKLOADS.values() if not w.backward]
+# Workloads small enough for the oracle to check every element of O and L
+# (the B=1 H=1 N=128 case and both masks of B=8 H=16 N=1024 d=64: 131072 rows).
+EVERY_ELEMENT = {"fwd_b1_h1_n128_d64_full", "fwd_b8_h16_n1024_d64_full",
+                 "fwd_b8_h16_n1024_d64_causal"}
 
 
 @pytest.mark.parametrize("w", FWD_WORKLOADS, ids=lambda w: w.name)
-def test_full_size_workloads_sampled_rows(w):
+def test_full_size_workloads(w):
+    # every workload at its stated seed, in the launch configuration the
+    # benchmark times; the small ones compared on every element, the others
+    # on >= 4096 rows spread over all heads
     print(f"[fwd full-size] {w.name}", flush=True)
     x = make_inputs(w.B, w.H, w.N, w.d, seed=w.seed, peaked_fraction=w.peaked_fraction)
     d = _dev(x)
@@ -235,18 +274,66 @@ def test_full_size_workloads_sampled_rows(w):
     binding.fa2_fwd(d["q"], d["k"], d["v"], o, lse, w.causal, w.scale)
     torch.cuda.synchronize()
     del d
-    rows = sample_rows(w.B, w.H, w.N)
-    o_ref, lse_ref = oracle.attention_forward_rows(x["q"], x["k"], x["v"], w.causal, w.scale,
-                                                   rows)
-    b, h, i = (torch.as_tensor(rows[:, c], device="cuda") for c in range(3))
-    o_got = o[b, i, h].cpu()
-    lse_got = lse[b, h, i].cpu()
-    rep = forward_report(o_got, lse_got, o_ref, lse_ref)
-    print(f"  {rep}", flush=True)
-    assert rep["ok"], rep
+    if w.name in EVERY_ELEMENT:
+        o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], w.causal, w.scale)
+        rep = forward_report(o.cpu(), lse.cpu(), o_ref, lse_ref)
+        print(f"  every element: {rep}", flush=True)
+        assert rep["ok"], rep
+    else:
+        check_rows(o, lse, x, w.causal, w.scale, spread_rows(w.B, w.H, w.N, seed=w.seed))
 
 
-@pytest.mark.parametrize("N", [600, 192, 100])
+# Causal shapes whose B*H is not a multiple of 8 reach the paired work
+# assignments of the forward dispatch (4-wave pairs at d = 64 and 128, 8-wave
+# pairs at d = 64) that the workloads above do not: every element of the
+# first and last head, and >= 4096 rows over all heads.
+DISPATCH_SHAPES = [(1, 9, 8192, 64), (1, 25, 16384, 64), (1, 9, 8192, 128)]
+
+
+@pytest.mark.parametrize("shape", DISPATCH_SHAPES, ids=lambda s: "b{}h{}n{}d{}".format(*s))
+def test_paired_causal_dispatch_shapes(shape):
+    B, H, N, d = shape
+    print(f"[fwd dispatch] shape={shape} causal=True variant="
+          f"{binding.fa2_variant_name(binding.fa2_fwd_variant(B, H, N, d, True))}", flush=True)
+    x = make_inputs(B, H, N, d, seed=29)
+    dx = _dev(x)
+    o = torch.empty_like(dx["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    binding.fa2_fwd(dx["q"], dx["k"], dx["v"], o, lse, True, d ** -0.5)
+    torch.cuda.synchronize()
+    del dx
+    whole = np.array([(b, h, i) for (b, h) in ((0, 0), (B - 1, H - 1)) for i in range(N)],
+                     dtype=np.int64)
+    check_rows(o, lse, x, True, d ** -0.5, whole)
+    check_rows(o, lse, x, True, d ** -0.5, spread_rows(B, H, N, seed=5))
+
+
+WIDE_N = [600, 192, 100]
+WIDE_BH = (2, 128)
+
+
+def fwd_parity_cases():
+    """(B, H, N, d, causal) of every fa2_fwd call the parity tests above
+    compare with the oracle."""
+    both = (False, True)
+    cases = [(*s, c) for s in SMALL_SHAPES for c in both]
+    cases += [(*SCALE_SHAPE, d, c) for d in (64, 128) for c in both]
+    cases += [(w.B, w.H, w.N, w.d, w.causal) for w in FWD_WORKLOADS]
+    cases += [(*s, True) for s in DISPATCH_SHAPES]
+    cases += [(*WIDE_BH, n, d, c) for n in WIDE_N for d in (64, 128) for c in both]
+    return cases
+
+
+def test_every_forward_configuration_is_compared_on_this_device():
+    # with this device's occupancy answer (the one fa2_fwd uses), every kernel
+    # configuration the dispatch can pick runs in at least one parity case
+    seen = {binding.fa2_fwd_variant(*c) for c in fwd_parity_cases()}
+    names = {v: binding.fa2_variant_name(v) for v in range(12)}
+    missing = [names[v] for v in names if v not in seen]
+    assert not missing, missing
+
+
+@pytest.mark.parametrize("N", WIDE_N)
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_wide_grid_ragged(d, causal, N):
@@ -255,7 +342,7 @@ def test_wide_grid_ragged(d, causal, N):
     # heavy and a light tile (or the middle tile alone).  The small shapes
     # above take the 4-wave tiles of small grids.  Each N ends the K/V loop
     # differently: ragged tail, two full tiles, one short tile.
-    B, H = 2, 128
+    B, H = WIDE_BH
     print(f"[fwd wide] B={B} H={H} N={N} d={d} causal={causal}", flush=True)
     x = make_inputs(B, H, N, d, seed=13)
     d_ = _dev(x)
@@ -342,7 +429,8 @@ def test_split_kv_zero_and_subnormal_scale(scale):
                                        ("fwd_b1_h2_n16384_d128_full", "split-kv"),
                                        ("fwd_b4_h16_n4096_d128_causal", "split-kv")])
 def test_other_forward_entry_points_full_size(name, algo):
-    # the ablation and split-KV entry points at full size, on sampled rows
+    # the ablation and split-KV entry points at full size, on >= 4096 rows
+    # spread over all heads
     w = WORKLOADS[name]
     print(f"[fwd full-size {algo}] {w.name}", flush=True)
     x = make_inputs(w.B, w.H, w.N, w.d, seed=w.seed, peaked_fraction=w.peaked_fraction)
@@ -353,10 +441,4 @@ def test_other_forward_entry_points_full_size(name, algo):
         o, lse = binding.attention_forward_split_kv(d["q"], d["k"], d["v"], w.causal, w.scale)
     torch.cuda.synchronize()
     del d
-    rows = sample_rows(w.B, w.H, w.N)
-    o_ref, lse_ref = oracle.attention_forward_rows(x["q"], x["k"], x["v"], w.causal, w.scale,
-                                                   rows)
-    b, h, i = (torch.as_tensor(rows[:, c], device="cuda") for c in range(3))
-    rep = forward_report(o[b, i, h].cpu(), lse[b, h, i].cpu(), o_ref, lse_ref)
-    print(f"  {rep}", flush=True)
-    assert rep["ok"], rep
+    check_rows(o, lse, x, w.causal, w.scale, spread_rows(w.B, w.H, w.N, seed=w.seed))
