@@ -64,7 +64,7 @@ __device__ __forceinline__ float swap_halves(float x) {
 // recognizer pads a VALU read of an MFMA result only when it can see the
 // instruction, and a hand-written v_max reading an accumulator right after
 // its MFMA was observed to see a partial sum (a race that only moved the
-// lazy-rescale reference, so results differed from run to run by rounding).
+// rescale reference, so results differed from run to run by rounding).
 // The NaN-propagating maximum lowers to a v_maximum3_f32 chain on gfx950
 // with no operand canonicalisation (fmaxf's IEEE maxNum quiets the first
 // operands with extra v_max instructions).  A NaN score makes the row max

@@ -10,7 +10,7 @@
 // (rescale by the old sum, add P V, divide by the new sum); and it can only
 // spread work over batch x heads.  This kernel does exactly that, and nothing
 // else differently from the shipping forward kernel: same MFMA mapping, same
-// LDS layout and DMA, the same exp2 softmax (without the lazy rescale), 32
+// LDS layout and DMA, the same exp2 softmax, 32
 // query rows per wave (the warp partition of section 4 is not part of this
 // ablation).  The O state
 // between steps is kept in fp32 in a caller workspace, so the result matches

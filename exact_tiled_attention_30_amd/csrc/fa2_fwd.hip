@@ -25,11 +25,20 @@
 //    one barrier per tile; see the kernel's comment for the LDS layout.
 //  * Softmax in base 2: t = s * scale*log2(e) in fp32 on the MFMA output
 //    (never folded into bf16 Q), P = exp2(t - m).  l is summed from the fp32
-//    P before the bf16 conversion.  The reference max m is only moved when a
-//    row's tile max exceeds it by more than kRescaleSlack (log2 units), so the
-//    O rescale (a multiply of every accumulator) is skipped on most tiles; the
-//    stored O/l and L = ln2 * (m + log2 l) are mathematically unchanged, and
-//    P stays <= 2^kRescaleSlack, far from fp32/bf16 overflow.
+//    P before the bf16 conversion.  The reference m of P = exp2(t - m) is
+//    the running row max, moved (with the O rescale: a multiply of every
+//    accumulator by exp2(m_old - m_new)) when a tile's max exceeds it -- with
+//    one exception that saves most rescales: a new max that would give a key
+//    at most 1/16 of the row's running sum, P <= l/16 (and at most 2^8), is
+//    left in P instead.  Any key that carries more of the row's mass moves m
+//    to its own score, so the largest P of a row dominated by a few keys is
+//    exactly 1, free of bf16 rounding, and O stays within rounding of those
+//    keys' V rows; a skipped key's P may be inexact in bf16 (2^-9
+//    relative), but its weight is at most 1/16.  (A reference allowed to
+//    trail the max by a fixed 8 whatever the mass put the dominant P's
+//    rounding into O: on the peaked N = 32768 workload that exceeded the O
+//    tolerance.)  O/l and L = ln2 * (m + log2 l) are mathematically the same
+//    for any reference.
 //  * Causal: K/V tiles past the Q tile's last row are never loaded; a wave
 //    skips tiles entirely above its rows; only tiles crossing the diagonal (or
 //    the ragged end of the sequence) run the element mask.
@@ -42,7 +51,14 @@
 namespace fa2 {
 namespace {
 
-constexpr float kRescaleSlack = 8.0f;
+// Threshold of the next rescale: the running max plus log2 of the lane's
+// running sum minus kMassShift (a new key of P <= l_lane / 2^kMassShift does
+// not move the reference), clamped to [0, kMaxSlack] so P stays <= 2^8.
+constexpr float kMassShift = 4.0f, kMaxSlack = 8.0f;
+__device__ __forceinline__ float next_threshold(float m_run, float l_lane) {
+  return m_run + __builtin_amdgcn_fmed3f(__builtin_amdgcn_logf(l_lane) - kMassShift, 0.0f,
+                                         kMaxSlack);
+}
 
 // ---------------------------------------------------------------------------
 // K and V tiles move HBM/L2 -> LDS with global_load_lds_dwordx4: lane L of a
@@ -190,8 +206,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
-  float m_run = -INFINITY;
-  float m_thr = -INFINITY;  // m_run + kRescaleSlack
+  float m_run = -INFINITY;  // reference max of P (log2 units)
+  float m_thr = -INFINITY;  // a tile max above this moves the reference
   float neg_mref = 0.f;     // -m_run, or 0 while m_run is -inf
   float l_part = 0.f;
 
@@ -242,7 +258,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
-      m_thr = m_run + kRescaleSlack;
       neg_mref = (m_run == -INFINITY) ? 0.f : -m_run;
     }
 
@@ -291,6 +306,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
       __builtin_amdgcn_sched_group_barrier(0x008, kM - (2 * kM - kAhead) / 2, 0);
     }
     l_part += rs;
+    m_thr = next_threshold(m_run, l_part);
   };
 
   // STAGES-deep LDS pipeline.  At step jt the DMA for tile jt+STAGES-1 is
@@ -511,12 +527,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
-  float m_run = -INFINITY;
-  float m_thr = -INFINITY;  // m_run + kRescaleSlack
+  float m_run = -INFINITY;  // reference max of P (log2 units)
+  float m_thr = -INFINITY;  // a tile max above this moves the reference
   float neg_mref = 0.f;     // -m_run, or 0 while m_run is -inf
   float l_part = 0.f;
-  // lazy rescale (see fwd_dl_kernel); returns minus the reference the tile's
-  // P uses
+  // move the reference when the tile's max passes the threshold (see the
+  // file comment); returns minus the reference the tile's P uses
   auto rescale_to = [&](float mt) __attribute__((always_inline)) {
     if (wave_any(mt > m_thr)) {
       const float m_new = fmaxf(m_run, mt);
@@ -525,7 +541,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
-      m_thr = m_run + kRescaleSlack;
       neg_mref = (m_run == -INFINITY) ? 0.f : -m_run;
     }
     return neg_mref;
@@ -611,6 +626,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
     pv(v_cur, pf);
     mt = tile_max(sn);
     l_part += rs;
+    m_thr = next_threshold(m_run, l_part);
     wait_dma_and_lds();
     __syncthreads();
   };
@@ -624,6 +640,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
     const float rs = probs(sc, nm, pf);
     pv(v_cur, pf);
     l_part += rs;
+    m_thr = next_threshold(m_run, l_part);
     wait_dma_and_lds();
     __syncthreads();
   };

@@ -92,12 +92,13 @@ def gradient_report(g, g_ref) -> dict:
         "ref_mean": ref_mean,
         "all_finite": bool(np.isfinite(g).all()),
     }
-    # An all-zero reference (e.g. scale = 0 makes dQ and dK exactly 0) is
-    # matched only by an all-zero result.
-    rep["max_rel"] = rep["max_abs"] / ref_max if ref_max > 0 else (
-        0.0 if rep["max_abs"] == 0.0 else float("inf"))
-    rep["mean_rel"] = rep["mean_abs"] / ref_mean if ref_mean > 0 else (
-        0.0 if rep["mean_abs"] == 0.0 else float("inf"))
+    # An all-zero reference (dQ and dK of a single visible key, where
+    # dS = P (dP - D) vanishes; any gradient at scale = 0) has no magnitude of
+    # its own: its errors are compared in absolute terms against the same
+    # numbers, so the fp32 rounding noise of dP - D passes and O(1) errors
+    # do not.
+    rep["max_rel"] = rep["max_abs"] / ref_max if ref_max > 0 else rep["max_abs"]
+    rep["mean_rel"] = rep["mean_abs"] / ref_mean if ref_mean > 0 else rep["mean_abs"]
     rep["ok"] = bool(rep["all_finite"] and rep["max_rel"] <= G_MAX_REL
                      and rep["mean_rel"] <= G_MEAN_REL)
     return rep

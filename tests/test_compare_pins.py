@@ -12,7 +12,8 @@ tests fix the checker to its stated bounds:
     |dL| <= 1e-3, max |dG| <= 5e-2 max |G_ref|, mean |dG| <= 5e-3 mean |G_ref|
     -- accepts a result 1e-9 (relative) inside it and rejects one 1e-9 past
     it, with errors of either sign, in several bf16 binades;
-  * NaN and infinity are rejected; an all-zero reference is met only by zeros;
+  * NaN and infinity are rejected; errors against an all-zero reference are
+    held to the same bounds in absolute terms;
   * a gradient reference below bf16's normal range is met by the exactly
     rounded result and missed by one 3/4 of a bf16 spacing off;
   * planted slips in a copy of the checker's source -- any bound loosened by
@@ -158,11 +159,15 @@ def pin_gradient_non_finite_and_zero_reference(m):
     g, ref = grad_arrays()
     g[0, 0, 0] = np.nan
     assert not m.gradient_report(g, ref)["ok"]
+    # an all-zero reference: absolute errors against the same bounds
     z = np.zeros((2, 8, 64))
     assert m.gradient_report(z, z)["ok"]
-    tiny = z.copy()
-    tiny[1, 2, 3] = 1e-30
-    assert not m.gradient_report(tiny, z)["ok"]
+    noise = z + 1e-7
+    assert m.gradient_report(noise, z)["ok"]
+    one = z.copy()
+    one[1, 2, 3] = G_MAX * PAST
+    assert not m.gradient_report(one, z)["ok"]
+    assert not m.gradient_report(z + G_MEAN * PAST, z)["ok"]
 
 
 def pin_gradient_subnormal_reference(m):
