@@ -5,7 +5,7 @@ turns torch tensors into device pointers and sizes, picks the current torch
 stream, and turns status codes into exceptions.  There is no fallback: if the
 library is missing the call fails loudly.
 
-Names mirror include/fa2.h: fa2_fwd, fa2_bwd, fa2_bwd_workspace_bytes,
+Names mirror include/fa2.h: fa2_fwd, fa2_bwd, fa2_bwd_workspace_bytes, fa2_bwd_noalloc,
 fa2_bwd_atomic_dq, fa2_bwd_atomic_dq_workspace_bytes, fa2_fwd_split_kv,
 fa2_fwd_split_kv_workspace_bytes, fa2_fwd_fa1_order, fa2_fwd_fa1_order_workspace_bytes,
 fa2_fwd_variant, fa2_bwd_variant, fa2_variant_name, fa2_calibrate_mfma, fa2_status_string.
@@ -50,6 +50,9 @@ def lib():
     L.fa2_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                           _i, _i, _i, _i, _i, ctypes.c_float, _vp]
     L.fa2_bwd.restype = _i
+    L.fa2_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                  _i, ctypes.c_float, _vp]
+    L.fa2_bwd_noalloc.restype = _i
     L.fa2_bwd_atomic_dq_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
     L.fa2_bwd_atomic_dq_workspace_bytes.restype = ctypes.c_size_t
     L.fa2_bwd_atomic_dq.argtypes = L.fa2_bwd.argtypes
@@ -243,6 +246,28 @@ def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool, scale: f
     device tensor of at least fa2_bwd_workspace_bytes(...) bytes.  Raises Fa2Error."""
     _check(lib().fa2_bwd(*_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, scale,
                                      stream)))
+
+
+BWD_NOALLOC_MAX_ROWS = 4194304  # FA2_BWD_NOALLOC_MAX_ROWS of include/fa2.h
+
+
+def fa2_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float,
+                    stream=None) -> None:
+    """Enqueue fa2_bwd with the library's static scratch instead of a
+    workspace: no device memory is allocated (B*H*N <= BWD_NOALLOC_MAX_ROWS;
+    calls overlapping on one GPU race).  Raises Fa2Error."""
+    import torch
+
+    B, N, H, d = _bnhd(q)
+    named = ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+             (dv, "dv"))
+    _shapes(named, lse, B, N, H, d)
+    for t, name in named:
+        _require(t, torch.bfloat16, name)
+    _require(lse, torch.float32, "lse")
+    _check(lib().fa2_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)),
+                                 float(scale), _stream(q, stream)))
 
 
 def fa2_bwd_atomic_dq(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool, scale: float,

@@ -76,6 +76,9 @@ const char* fa2_status_string(int status) {
     case FA2_ERR_ALIAS: return "FA2_ERR_ALIAS: an output overlaps another tensor";
     case FA2_ERR_WORKSPACE: return "FA2_ERR_WORKSPACE: workspace missing or too small";
     case FA2_ERR_LAUNCH: return "FA2_ERR_LAUNCH: the HIP runtime rejected a launch";
+    case FA2_ERR_SCRATCH:
+      return "FA2_ERR_SCRATCH: B*H*N exceeds FA2_BWD_NOALLOC_MAX_ROWS, the rows the static "
+             "scratch of fa2_bwd_noalloc holds";
     default: return "unknown fa2 status";
   }
 }
@@ -196,6 +199,43 @@ size_t fa2_bwd_atomic_dq_workspace_bytes(int B, int H, int N, int d, int causal)
 
 }  // extern "C"
 
+namespace fa2 {
+
+// Host checks of a backward call, in the order fa2_bwd makes them: shapes,
+// then (for a non-empty problem) pointers, the workspace (need_ws bytes;
+// kNoWorkspace when the call takes none), alignment and overlaps.
+int bwd_checks(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, size_t need_ws, int B, int H, int N, int d, float scale,
+               size_t* rows_out) {
+  size_t elems = 0, rows = 0;
+  const int st = check_shape(B, H, N, d, scale, &elems, &rows);
+  *rows_out = rows;
+  if (st != FA2_OK) return st;
+  if (elems == 0) return FA2_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA2_ERR_NULLPTR;
+  const bool has_ws = need_ws != kNoWorkspace;
+  if (has_ws && (!workspace || workspace_bytes < need_ws)) return FA2_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || (has_ws && !aligned(workspace, 16)))
+    return FA2_ERR_ALIGN;
+  const size_t tb = elems * 2, lb = rows * sizeof(float);
+  const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb),
+                       range_of(lse, lb), range_of(dout, tb)};
+  const Range outs[] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
+                        has_ws ? range_of(workspace, workspace_bytes) : Range{0, 0}};
+  for (const Range& out : outs)
+    for (const Range& in : ins)
+      if (overlap(out, in)) return FA2_ERR_ALIAS;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return FA2_ERR_ALIAS;
+  return FA2_OK;
+}
+
+}  // namespace fa2
+
 namespace {
 
 // Shared argument checks and launch of the two backward entry points.
@@ -203,30 +243,12 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
                const void* dout, void* dq, void* dk, void* dv, void* workspace,
                size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
                void* stream, bool atomic_dq) {
-  size_t elems = 0, rows = 0;
-  const int st = check_shape(B, H, N, d, scale, &elems, &rows);
-  if (st != FA2_OK) return st;
-  if (elems == 0) return FA2_OK;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA2_ERR_NULLPTR;
   const size_t need = atomic_dq ? fa2_bwd_atomic_dq_workspace_bytes(B, H, N, d, causal)
                                 : fa2_bwd_workspace_bytes(B, H, N, d, causal);
-  if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4) || !aligned(workspace, 16))
-    return FA2_ERR_ALIGN;
-  const size_t tb = elems * 2, lb = rows * sizeof(float);
-  const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb),
-                       range_of(lse, lb), range_of(dout, tb)};
-  const Range outs[] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
-                        range_of(workspace, workspace_bytes)};
-  for (const Range& out : outs)
-    for (const Range& in : ins)
-      if (overlap(out, in)) return FA2_ERR_ALIAS;
-  for (int i = 0; i < 4; ++i)
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outs[j])) return FA2_ERR_ALIAS;
-
+  size_t rows = 0;
+  const int st = fa2::bwd_checks(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                                 need, B, H, N, d, scale, &rows);
+  if (st != FA2_OK || rows == 0) return st;
   char* ws = (char*)workspace;
   fa2::BwdParams p{q, k, v, o, lse, dout, dq, dk, dv,
                    (float*)ws, atomic_dq ? (float*)(ws + fa2::bwd_delta_bytes(B, H, N)) : nullptr,

@@ -81,6 +81,14 @@ struct Fa1Params {
   hipStream_t stream;
 };
 
+// Host argument checks of a backward call (fa2_api.cpp); need_ws is the
+// workspace size the call requires, or kNoWorkspace when it takes none.
+constexpr size_t kNoWorkspace = ~(size_t)0;
+int bwd_checks(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, size_t need_ws, int B, int H, int N, int d, float scale,
+               size_t* rows_out);
+
 // Workspace layout of the backward pass (offsets in bytes, 256-aligned).
 size_t bwd_delta_bytes(int B, int H, int N);
 size_t bwd_dq_acc_bytes(int B, int H, int N, int d);

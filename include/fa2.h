@@ -55,7 +55,8 @@ typedef enum fa2_status {
   FA2_ERR_ALIGN = 5,     /* a base pointer is not 16-byte (lse: 4-byte) aligned   */
   FA2_ERR_ALIAS = 6,     /* an output range overlaps an input or another output   */
   FA2_ERR_WORKSPACE = 7, /* backward workspace missing or smaller than required   */
-  FA2_ERR_LAUNCH = 8     /* the HIP runtime rejected a kernel launch              */
+  FA2_ERR_LAUNCH = 8,    /* the HIP runtime rejected a kernel launch              */
+  FA2_ERR_SCRATCH = 9    /* fa2_bwd_noalloc: B*H*N above FA2_BWD_NOALLOC_MAX_ROWS */
 } fa2_status;
 
 /*
@@ -100,6 +101,32 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o,
             const float* lse, const void* dout, void* dq, void* dk, void* dv,
             void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
             int causal, float scale, void* stream);
+
+/* Rows B*H*N fa2_bwd_noalloc serves: its static scratch holds one fp32 D
+ * value per row (16 MiB on each GPU the library runs on). */
+#define FA2_BWD_NOALLOC_MAX_ROWS 4194304
+
+/*
+ * fa2_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels and results as fa2_bwd (bitwise), but the D vector lives in a
+ * scratch array of the library's own, allocated with the code object
+ * (FA2_BWD_NOALLOC_MAX_ROWS fp32 values per GPU, held until the process
+ * ends), so the caller passes no workspace and nothing is allocated:
+ * no hipMalloc, hipFree or allocating library call on any path.
+ *   Arguments, layouts, ownership and errors as for fa2_bwd, without the
+ *   workspace; B*H*N > FA2_BWD_NOALLOC_MAX_ROWS returns FA2_ERR_SCRATCH
+ *   before any HIP call.  The scratch of a GPU is looked up once per device
+ *   (hipGetSymbolAddress, with the stream's device current).
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (on different streams, or from several threads) race and
+ *   must be ordered by the caller.  Nothing in the scratch needs to start at
+ *   zero (each call writes every D value it reads); its contents after a
+ *   call are the last call's D.
+ */
+int fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    int B, int H, int N, int d, int causal, float scale, void* stream);
 
 /*
  * Bytes of device workspace fa2_bwd_atomic_dq needs (0 if the problem is

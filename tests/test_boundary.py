@@ -16,7 +16,7 @@ from exact_tiled_attention_30_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa2.h")
 
-OK, NULLPTR, SHAPE, HEADDIM, SCALE, ALIGN, ALIAS, WORKSPACE, LAUNCH = range(9)
+OK, NULLPTR, SHAPE, HEADDIM, SCALE, ALIGN, ALIAS, WORKSPACE, LAUNCH, SCRATCH = range(10)
 
 # Fake, well-aligned, non-overlapping "device" addresses.  Only argument
 # checks run with them: every call below fails validation or is empty.
@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa2_bwd", "fa2_bwd_atomic_dq",
-                                    "fa2_bwd_atomic_dq_workspace_bytes",
+                                    "fa2_bwd_atomic_dq_workspace_bytes", "fa2_bwd_noalloc",
                                     "fa2_bwd_variant", "fa2_bwd_workspace_bytes",
                                     "fa2_calibrate_mfma", "fa2_fwd", "fa2_fwd_fa1_order",
                                     "fa2_fwd_fa1_order_workspace_bytes", "fa2_fwd_split_kv",
@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(9):
+    for s in range(10):
         msg = binding.fa2_status_string(s)
         assert msg.startswith("FA2_")
     assert binding.fa2_status_string(OK) == "FA2_OK"
@@ -147,6 +147,32 @@ def test_bwd_argument_errors(L, atomic):
     assert bwd(L, dv=DQ + 64, atomic=atomic) == ALIAS
     assert bwd(L, ws=DO, atomic=atomic) == ALIAS
     assert bwd(L, N=0, q=None, ws=None, atomic=atomic) == OK
+
+
+def noalloc(L, B=2, H=3, N=100, d=64, causal=1, scale=0.125, **ptrs):
+    p = dict(q=Q, k=K, v=V, o=O, lse=LSE, dout=DO, dq=DQ, dk=DK, dv=DV)
+    p.update(ptrs)
+    return L.fa2_bwd_noalloc(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"],
+                             p["dk"], p["dv"], B, H, N, d, causal, ctypes.c_float(scale), None)
+
+
+def test_bwd_noalloc_argument_errors(L):
+    # fa2_bwd's checks without a workspace, then the static scratch's limit;
+    # every case returns before any HIP call
+    assert noalloc(L, N=-1) == SHAPE
+    assert noalloc(L, d=32) == HEADDIM
+    assert noalloc(L, scale=math.nan) == SCALE
+    for name in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv"):
+        assert noalloc(L, **{name: None}) == NULLPTR, name
+    assert noalloc(L, dq=DQ + 4) == ALIGN
+    assert noalloc(L, dk=K) == ALIAS
+    assert noalloc(L, dv=DQ + 64) == ALIAS
+    # one row past FA2_BWD_NOALLOC_MAX_ROWS (4 Mi rows of D, 16 MiB)
+    assert binding.BWD_NOALLOC_MAX_ROWS == 4194304
+    assert noalloc(L, B=1, H=1, N=4194305) == SCRATCH
+    assert noalloc(L, B=2, H=4, N=524289, causal=0) == SCRATCH
+    assert "FA2_BWD_NOALLOC_MAX_ROWS" in binding.fa2_status_string(SCRATCH)
+    assert noalloc(L, N=0, q=None) == OK
 
 
 def test_atomic_workspace_is_larger(L):
