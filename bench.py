@@ -98,9 +98,12 @@ def parse_args():
                    help="a workload name, or two forward workloads on the same inputs "
                         "joined by '+'")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    p.add_argument("--algo", choices=("fa2", "split-kv", "fa1-order"), default="fa2",
+    p.add_argument("--algo", choices=("fa2", "split-kv", "fa1-order", "fa1-split-k"),
+                   default="fa2",
                    help="forward workloads: fa2_fwd, fa2_fwd_split_kv (library's slice "
-                        "count), or the FlashAttention-1-order ablation fa2_fwd_fa1_order")
+                        "count), or the FlashAttention-1-order ablation fa2_fwd_fa1_order "
+                        "with split-Q waves (fa1-order) or FlashAttention-1's split-K waves "
+                        "(fa1-split-k)")
     p.add_argument("--bwd-dq", choices=("two-pass", "atomic"), default="two-pass",
                    help="dQ strategy of a backward workload: fa2_bwd (a Q-outer dQ pass) "
                         "or fa2_bwd_atomic_dq (fp32 atomics)")
@@ -232,10 +235,10 @@ def main():
     import torch
 
     from exact_tiled_attention_30_amd import binding
-    from exact_tiled_attention_30_amd.inputs import WORKLOADS, inputs_for
+    from exact_tiled_attention_30_amd.inputs import inputs_for, workload
 
     names = tuple(args.workload.split("+"))
-    ws = [WORKLOADS[n] for n in names]
+    ws = [workload(n) for n in names]
     base = ws[0]
     for w in ws[1:]:
         assert (w.B, w.H, w.N, w.d) == (base.B, base.H, base.N, base.d)
@@ -258,13 +261,14 @@ def main():
             def fwd(w=w, sws=sws):
                 binding.fa2_fwd_split_kv(x["q"], x["k"], x["v"], o, lse, sws, w.causal, w.scale, 0)
             launches.append((w.name, fwd, w.flops()))
-        elif not w.backward and args.algo == "fa1-order":
+        elif not w.backward and args.algo in ("fa1-order", "fa1-split-k"):
             fws = torch.empty(binding.fa2_fwd_fa1_order_workspace_bytes(w.B, w.H, w.N, w.d,
                                                                         w.causal),
                               dtype=torch.uint8, device=dev)
 
             def fwd(w=w, fws=fws):
-                binding.fa2_fwd_fa1_order(x["q"], x["k"], x["v"], o, lse, fws, w.causal, w.scale)
+                binding.fa2_fwd_fa1_order(x["q"], x["k"], x["v"], o, lse, fws, w.causal, w.scale,
+                                          args.algo == "fa1-split-k")
             launches.append((w.name, fwd, w.flops()))
         elif not w.backward and args.cold:
             # a second input set (the same recipe, every value negated: the

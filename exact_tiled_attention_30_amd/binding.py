@@ -65,7 +65,7 @@ def lib():
     L.fa2_fwd_fa1_order_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
     L.fa2_fwd_fa1_order_workspace_bytes.restype = ctypes.c_size_t
     L.fa2_fwd_fa1_order.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i, _i, _i, _i,
-                                    _i, ctypes.c_float, _vp]
+                                    _i, ctypes.c_float, _i, _vp]
     L.fa2_fwd_fa1_order.restype = _i
     L.fa2_calibrate_mfma.argtypes = [_vp, _i, _i, _vp]
     L.fa2_calibrate_mfma.restype = _i
@@ -203,17 +203,19 @@ def fa2_fwd_fa1_order_workspace_bytes(B: int, H: int, N: int, d: int, causal: bo
 
 
 def fa2_fwd_fa1_order(q, k, v, o, lse, workspace, causal: bool, scale: float,
-                      stream=None) -> None:
-    """Enqueue the forward pass in FlashAttention-1's loop order (an ablation).
-    workspace: a uint8 device tensor of at least
-    fa2_fwd_fa1_order_workspace_bytes(...) bytes.  Raises Fa2Error."""
+                      split_k: bool = False, stream=None) -> None:
+    """Enqueue the forward pass in FlashAttention-1's loop order (an ablation);
+    split_k: FlashAttention-1's own wave partition (waves split each K/V tile
+    and merge through LDS) instead of FlashAttention-2's split-Q.  workspace:
+    a uint8 device tensor of at least fa2_fwd_fa1_order_workspace_bytes(...)
+    bytes.  Raises Fa2Error."""
     import torch
 
     B, N, H, d = _fwd_checks(q, k, v, o, lse)
     _require(workspace, torch.uint8, "workspace")
     _check(lib().fa2_fwd_fa1_order(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
                                    workspace.numel(), B, H, N, d, int(bool(causal)), float(scale),
-                                   _stream(q, stream)))
+                                   int(bool(split_k)), _stream(q, stream)))
 
 
 def fa2_bwd_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
@@ -309,7 +311,8 @@ def attention_forward_split_kv(q, k, v, causal: bool = False, scale: float | Non
     return o, lse
 
 
-def attention_forward_fa1_order(q, k, v, causal: bool = False, scale: float | None = None):
+def attention_forward_fa1_order(q, k, v, causal: bool = False, scale: float | None = None,
+                                split_k: bool = False):
     """Allocate O, L and the workspace, run fa2_fwd_fa1_order, return (o, lse)."""
     import torch
 
@@ -320,7 +323,7 @@ def attention_forward_fa1_order(q, k, v, causal: bool = False, scale: float | No
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     ws = torch.empty(max(1, fa2_fwd_fa1_order_workspace_bytes(B, H, N, d, causal)),
                      dtype=torch.uint8, device=q.device)
-    fa2_fwd_fa1_order(q, k, v, o, lse, ws, causal, scale)
+    fa2_fwd_fa1_order(q, k, v, o, lse, ws, causal, scale, split_k)
     return o, lse
 
 

@@ -156,7 +156,7 @@ size_t fa2_fwd_fa1_order_workspace_bytes(int B, int H, int N, int d, int causal)
 
 int fa2_fwd_fa1_order(const void* q, const void* k, const void* v, void* o, float* lse,
                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
-                      int causal, float scale, void* stream) {
+                      int causal, float scale, int split_k, void* stream) {
   size_t elems = 0, rows = 0;
   const int st = check_shape(B, H, N, d, scale, &elems, &rows);
   if (st != FA2_OK) return st;
@@ -180,6 +180,7 @@ int fa2_fwd_fa1_order(const void* q, const void* k, const void* v, void* o, floa
   fa2::Fa1Params p{q, k, v, o, lse, (float*)ws,
                    (float*)(ws + fa2::bwd_dq_acc_bytes(B, H, N, d)), B, H, N, d, causal != 0,
                    scale, (hipStream_t)stream};
+  p.split_k = split_k != 0;
   return fa2::launch_fa1_order_fwd(p) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 

@@ -79,6 +79,7 @@ struct Fa1Params {
   bool causal;
   float scale;
   hipStream_t stream;
+  bool split_k = false;  // FlashAttention-1's split-K wave partition (else split-Q)
 };
 
 // Host argument checks of a backward call (fa2_api.cpp); need_ws is the

@@ -95,6 +95,21 @@ def make_inputs_on_device(B: int, H: int, N: int, d: int, seed: int = 0,
     return out
 
 
+def workload(name: str) -> Workload:
+    """A named workload, or one spelled fwd_b{B}_h{H}_n{N}_d{d}_{full|causal}
+    (or bwd_...) with the default recipe (seed 0, no peaked rows)."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    import re
+
+    m = re.fullmatch(r"(fwd|bwd)_b(\d+)_h(\d+)_n(\d+)_d(\d+)_(full|causal)", name)
+    if not m:
+        raise KeyError(f"unknown workload {name!r}")
+    kind, B, H, N, d, mask = m.groups()
+    return Workload(name, int(B), int(H), int(N), int(d), mask == "causal",
+                    backward=kind == "bwd")
+
+
 def inputs_for(w: Workload):
     return make_inputs(w.B, w.H, w.N, w.d, seed=w.seed,
                        peaked_fraction=w.peaked_fraction, with_dout=w.backward)

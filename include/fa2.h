@@ -188,17 +188,24 @@ size_t fa2_fwd_fa1_order_workspace_bytes(int B, int H, int N, int d, int causal)
  * The forward pass in FlashAttention-1's loop order, kept to measure what
  * FlashAttention-2's changes buy ("FlashAttention Implementation >
  * FlashAttention-2 Improvements"; "6.2 FlashAttention V2 in depth", sections
- * 2.1 and 3.1-3.3): K/V tiles in the outer loop and Q tiles in the inner
+ * 2.1 and 3.1-3.4): K/V tiles in the outer loop and Q tiles in the inner
  * one, the Q tile reloaded and the O tile and its row statistics read and
  * written back (in the fp32 workspace) at every step, O renormalised after
- * every step, and one workgroup per (batch, head).  Same inputs, outputs,
- * layouts, ownership and errors as fa2_fwd, plus the workspace (at least
- * fa2_fwd_fa1_order_workspace_bytes() bytes, 16-byte aligned, contents on
- * entry ignored and overwritten).
+ * every step, and one workgroup per (batch, head).
+ *   split_k = 0: the waves of a workgroup own query rows (FlashAttention-2's
+ *                split-Q partition, section 4.2), so only the loop order and
+ *                the per-step renormalisation differ from fa2_fwd;
+ *   split_k != 0: FlashAttention-1's own partition (sections 4.1, 4.3): the
+ *                waves share the Q rows and split each K/V tile, and their
+ *                partial softmax results (max, sum, P V) are merged through
+ *                LDS at every step.
+ * Same inputs, outputs, layouts, ownership and errors as fa2_fwd, plus the
+ * workspace (at least fa2_fwd_fa1_order_workspace_bytes() bytes, 16-byte
+ * aligned, contents on entry ignored and overwritten).
  */
 int fa2_fwd_fa1_order(const void* q, const void* k, const void* v, void* o, float* lse,
                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
-                      int causal, float scale, void* stream);
+                      int causal, float scale, int split_k, void* stream);
 
 /* Measurement helper, not part of the attention path: runs `blocks`
  * workgroups of 256 threads in which every wave issues iters x 4

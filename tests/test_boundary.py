@@ -186,7 +186,7 @@ def fa1(L, q=Q, k=K, v=V, o=O, lse=LSE, ws=WS, ws_bytes=None, B=2, H=3, N=100, d
     if ws_bytes is None:
         ws_bytes = L.fa2_fwd_fa1_order_workspace_bytes(B, H, N, d, causal)
     return L.fa2_fwd_fa1_order(q, k, v, o, lse, ws, ws_bytes, B, H, N, d, causal,
-                               ctypes.c_float(scale), None)
+                               ctypes.c_float(scale), 0, None)
 
 
 def test_fa1_order_argument_errors(L):

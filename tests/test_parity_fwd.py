@@ -185,13 +185,14 @@ def test_forward_is_bitwise_deterministic(causal, d):
         assert torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("algo", ["split_kv", "fa1_order"])
+@pytest.mark.parametrize("algo", ["split_kv", "fa1_order", "fa1_order_split_k"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_other_forwards_are_bitwise_deterministic(algo, causal, d):
     # split-KV merges its slices in a fixed order and FA-1 order owns each
-    # head in one workgroup: neither uses atomics, so repeated runs on a grid
-    # that fills the GPU must agree to the bit
+    # head in one workgroup (its split-K waves merge in a fixed order):
+    # none uses atomics, so repeated runs on a grid that fills the GPU must
+    # agree to the bit
     B, H, N = 2, 16, 2048 if algo == "split_kv" else 1024
     x = _dev(make_inputs(B, H, N, d, seed=17))
     if algo == "split_kv":
@@ -199,7 +200,7 @@ def test_other_forwards_are_bitwise_deterministic(algo, causal, d):
                                                          d ** -0.5, 4)
     else:
         run = lambda: binding.attention_forward_fa1_order(x["q"], x["k"], x["v"], causal,
-                                                          d ** -0.5)
+                                                          d ** -0.5, algo.endswith("split_k"))
     o1, l1 = run()
     for _ in range(3):
         o2, l2 = run()
@@ -366,26 +367,35 @@ FA1_SHAPES = [(1, 1, 128, 64), (2, 3, 200, 64), (1, 2, 333, 128), (1, 1, 1000, 6
               (1, 1, 1, 128), (2, 2, 520, 128)]
 
 
+# split_k: FlashAttention-1's own wave partition (waves split each K/V tile
+# and merge their partial softmax through LDS); else the split-Q waves
+PARTITIONS = [False, True]
+PARTITION_IDS = ["split_q", "split_k"]
+
+
+@pytest.mark.parametrize("split_k", PARTITIONS, ids=PARTITION_IDS)
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("shape", FA1_SHAPES, ids=lambda s: "b{}h{}n{}d{}".format(*s))
-def test_fa1_order_every_element(shape, causal):
+def test_fa1_order_every_element(shape, causal, split_k):
     B, H, N, d = shape
     x = make_inputs(B, H, N, d, seed=17)
-    print(f"[fa1-order] shape={shape} causal={causal}", flush=True)
+    print(f"[fa1-order] shape={shape} causal={causal} split_k={split_k}", flush=True)
     dx = _dev(x)
-    o, lse = binding.attention_forward_fa1_order(dx["q"], dx["k"], dx["v"], causal, d ** -0.5)
+    o, lse = binding.attention_forward_fa1_order(dx["q"], dx["k"], dx["v"], causal, d ** -0.5,
+                                                 split_k)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], causal, d ** -0.5)
     rep = forward_report(o.cpu(), lse.cpu(), o_ref, lse_ref)
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("split_k", PARTITIONS, ids=PARTITION_IDS)
 @pytest.mark.parametrize("scale", [0.0, -0.125, 1e-40])
-def test_fa1_order_unusual_scales(scale):
+def test_fa1_order_unusual_scales(scale, split_k):
     B, H, N, d = 1, 2, 300, 64
     x = make_inputs(B, H, N, d, seed=5)
     dx = _dev(x)
-    o, lse = binding.attention_forward_fa1_order(dx["q"], dx["k"], dx["v"], True, scale)
+    o, lse = binding.attention_forward_fa1_order(dx["q"], dx["k"], dx["v"], True, scale, split_k)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_forward(x["q"], x["k"], x["v"], True, scale)
     rep = forward_report(o.cpu(), lse.cpu(), o_ref, lse_ref)
@@ -426,6 +436,8 @@ def test_split_kv_zero_and_subnormal_scale(scale):
 
 
 @pytest.mark.parametrize("name,algo", [("fwd_b8_h16_n1024_d64_causal", "fa1-order"),
+                                       ("fwd_b8_h16_n1024_d64_full", "fa1-split-k"),
+                                       ("fwd_b8_h16_n2048_d128_causal", "fa1-split-k"),
                                        ("fwd_b1_h2_n16384_d128_full", "split-kv"),
                                        ("fwd_b4_h16_n4096_d128_causal", "split-kv")])
 def test_other_forward_entry_points_full_size(name, algo):
@@ -435,8 +447,9 @@ def test_other_forward_entry_points_full_size(name, algo):
     print(f"[fwd full-size {algo}] {w.name}", flush=True)
     x = make_inputs(w.B, w.H, w.N, w.d, seed=w.seed, peaked_fraction=w.peaked_fraction)
     d = _dev(x)
-    if algo == "fa1-order":
-        o, lse = binding.attention_forward_fa1_order(d["q"], d["k"], d["v"], w.causal, w.scale)
+    if algo.startswith("fa1"):
+        o, lse = binding.attention_forward_fa1_order(d["q"], d["k"], d["v"], w.causal, w.scale,
+                                                     algo == "fa1-split-k")
     else:
         o, lse = binding.attention_forward_split_kv(d["q"], d["k"], d["v"], w.causal, w.scale)
     torch.cuda.synchronize()
