@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libfa2.so")
 
-SOURCES = ["fa2_api.cpp", "fa2_fwd.hip", "fa2_bwd.hip", "fa2_fa1_order.hip", "fa2_calib.hip",
+SOURCES = ["fa2_api.cpp", "fa2_dispatch.cpp", "fa2_fwd.hip", "fa2_bwd.hip", "fa2_fa1_order.hip", "fa2_calib.hip",
            "fa2_noalloc.hip"]
 
 HIPCC_FLAGS = [

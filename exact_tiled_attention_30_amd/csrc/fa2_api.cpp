@@ -14,6 +14,7 @@ namespace {
 
 constexpr size_t kMaxElems = (size_t)1 << 62;
 constexpr long long kMaxTokenElems = 1LL << 23;  // H * d of one token
+constexpr int kMaxN = 1 << 30;                   // tokens per sequence
 constexpr int kMaxSplits = 64;  // split-KV slices per Q tile
 
 struct Range {
@@ -31,7 +32,9 @@ bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
 // Shape checks shared by both passes.  *elems receives B*N*H*d.
 int check_shape(int B, int H, int N, int d, float scale, size_t* elems, size_t* rows) {
-  if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
+  // N <= 2^30 keeps every token index the kernels and launchers form (a
+  // tile's first row plus a tile, N rounded up to a tile) inside int
+  if (B < 0 || H < 0 || N < 0 || N > kMaxN) return FA2_ERR_SHAPE;
   if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
   // the kernels work with scale * log2(e), which must be a finite fp32 too
   if (!isfinite(scale) || !isfinite((float)((double)scale * 1.4426950408889634)))
@@ -69,7 +72,8 @@ const char* fa2_status_string(int status) {
   switch (status) {
     case FA2_OK: return "FA2_OK";
     case FA2_ERR_NULLPTR: return "FA2_ERR_NULLPTR: a required pointer is NULL";
-    case FA2_ERR_SHAPE: return "FA2_ERR_SHAPE: negative or too large B, H or N, or H*d above 2^23";
+    case FA2_ERR_SHAPE:
+      return "FA2_ERR_SHAPE: negative or too large B, H or N (N above 2^30), or H*d above 2^23";
     case FA2_ERR_HEADDIM: return "FA2_ERR_HEADDIM: head dimension must be 64 or 128";
     case FA2_ERR_SCALE: return "FA2_ERR_SCALE: scale and scale*log2(e) must be finite fp32 values";
     case FA2_ERR_ALIGN: return "FA2_ERR_ALIGN: tensor base pointer misaligned";

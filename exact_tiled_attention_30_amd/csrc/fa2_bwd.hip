@@ -1079,33 +1079,6 @@ hipError_t launch_bwd_two_pass(const BwdParams& p) {
 
 }  // namespace
 
-// Waves per workgroup of the dQ pass: 8 (256-row Q tiles), or 4 when the
-// 8-wave grid would give fewer than two workgroups per CU.
-int bwd_dq_waves(int B, int H, int N, bool causal) {
-  constexpr long long kCus = 256;
-  const long long items8 =
-      (long long)B * H * (causal ? ((N + 255) / 256 + 1) / 2 : (N + 255) / 256);
-  return items8 < 2 * kCus ? 4 : 8;
-}
-
-int bwd_variant(int B, int H, int N, int d, bool causal) {
-  const int w8 = bwd_dq_waves(B, H, N, causal) == 8;
-  return kBwdFirst + ((d == 128) << 2) + ((int)causal << 1) + w8;
-}
-
-const char* bwd_variant_name(int v) {
-  static const char* const names[8] = {
-      "bwd_dq_kernel<64,4,false>+bwd_dl_kernel<64,false,false>",
-      "bwd_dq_kernel<64,8,false>+bwd_dl_kernel<64,false,false>",
-      "bwd_dq_kernel<64,4,true>+bwd_dl_kernel<64,true,false>",
-      "bwd_dq_kernel<64,8,true>+bwd_dl_kernel<64,true,false>",
-      "bwd_dq_kernel<128,4,false>+bwd_kv_pair_kernel<128,false>",
-      "bwd_dq_kernel<128,8,false>+bwd_kv_pair_kernel<128,false>",
-      "bwd_dq_kernel<128,4,true>+bwd_kv_pair_kernel<128,true>",
-      "bwd_dq_kernel<128,8,true>+bwd_kv_pair_kernel<128,true>"};
-  return v >= kBwdFirst && v < kBwdFirst + 8 ? names[v - kBwdFirst] : nullptr;
-}
-
 hipError_t launch_bwd(const BwdParams& p) {
   if (p.d == 64)
     return p.causal ? launch_bwd_two_pass<64, true>(p) : launch_bwd_two_pass<64, false>(p);

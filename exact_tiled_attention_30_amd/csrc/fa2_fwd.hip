@@ -768,67 +768,6 @@ hipError_t launch_split_t(const FwdParams& p) {
 
 }  // namespace
 
-// Kernel configuration of the forward pass for a problem.  Tile shapes (K/V
-// tile 64 keys; 8 waves = 256-row Q tiles, or 4 waves = 128 rows) chosen by
-// measurement on MI355X, each parity-tested.  Grids of fewer 8-wave Q tiles
-// than CUs use 4-wave tiles (twice the workgroups); causal grids of fewer
-// than two 8-wave workgroups per CU use the 4-wave tiles too, and grids of
-// fewer 4-wave pairs than CUs drop the pairing.  Causal grids with whole
-// heads per XCD run one 4-wave workgroup per Q tile, dealt to the CUs by
-// weight (d = 128: only when the CUs hold the whole grid at once, i.e. when
-// B*H*ceil(N/128) <= 256 * resident_d128, the workgroups of that kernel one
-// CU holds).  Host-only arithmetic: the same answer with or without a GPU.
-int fwd_variant(int B, int H, int N, int d, bool causal, int resident_d128) {
-  constexpr long long kCus = 256;
-  if (!causal) {
-    // d = 128: the software-pipelined kernel (the VALU work of one tile under
-    // the MFMAs of the next); at d = 64 the plain kernel measures faster
-    const bool tiny = (long long)B * H * ((N + 255) / 256) < kCus;
-    if (d == 64) return tiny ? kFwdD64Nc4 : kFwdD64Nc8;
-    return tiny ? kFwdD128Sp4 : kFwdD128Sp8;
-  }
-  const long long pairs8 = (long long)B * H * (((N + 255) / 256 + 1) / 2);
-  const long long nq4 = (N + 127) / 128;
-  const long long pairs4 = (long long)B * H * ((nq4 + 1) / 2);
-  const long long tiles4 = (long long)B * H * nq4;
-  const bool small = pairs8 < 2 * kCus;
-  const bool tiny = pairs4 < kCus;  // 4-wave pairs would leave CUs idle: one tile each
-  // One 4-wave workgroup per Q tile, dealt to the CUs by weight: twice the
-  // waves of the pairs with the same balance when the grid is resident at
-  // once; on larger grids the first round is dealt the same way and later
-  // workgroups, still heaviest first, go wherever a slot frees.  At d = 64
-  // that beats the pairs on every causal workload measured (1-5 % past one
-  // round); at d = 128 only within one round (past it, 4-5 % slower at
-  // N >= 8192).
-  const bool whole_heads = nq4 > 0 && tiles4 % 8 == 0 && (tiles4 / 8) % nq4 == 0;
-  if (d == 64) {
-    if (whole_heads) return kFwdD64CausalDealt;
-    if (tiny) return kFwdD64CausalOne;
-    return small ? kFwdD64CausalPair4 : kFwdD64CausalPair8;
-  }
-  if (whole_heads && tiles4 <= kCus * resident_d128) return kFwdD128CausalDealt;
-  if (tiny) return kFwdD128CausalOne;
-  return small ? kFwdD128CausalPair4 : kFwdD128CausalPair8;
-}
-
-const char* fwd_variant_name(int v) {
-  switch (v) {
-    case kFwdD64Nc4: return "fwd_dl_kernel<64,64,4,2,false>";
-    case kFwdD64Nc8: return "fwd_dl_kernel<64,64,8,2,false>";
-    case kFwdD128Sp4: return "fwd_sp_kernel<128,64,4>";
-    case kFwdD128Sp8: return "fwd_sp_kernel<128,64,8>";
-    case kFwdD64CausalDealt: return "fwd_dl_kernel<64,64,4,2,true,false,false,true>";
-    case kFwdD64CausalOne: return "fwd_dl_kernel<64,64,4,2,true,false,false>";
-    case kFwdD64CausalPair4: return "fwd_dl_kernel<64,64,4,2,true>";
-    case kFwdD64CausalPair8: return "fwd_dl_kernel<64,64,8,2,true>";
-    case kFwdD128CausalDealt: return "fwd_dl_kernel<128,64,4,2,true,false,false,true>";
-    case kFwdD128CausalOne: return "fwd_dl_kernel<128,64,4,2,true,false,false>";
-    case kFwdD128CausalPair4: return "fwd_dl_kernel<128,64,4,2,true>";
-    case kFwdD128CausalPair8: return "fwd_dl_kernel<128,64,8,2,true>";
-    default: return nullptr;
-  }
-}
-
 int fwd_resident_d128() { return resident_wgs<128, 64, 4, 2, true, false, true>(); }
 
 hipError_t launch_fwd(const FwdParams& p) {
@@ -847,19 +786,6 @@ hipError_t launch_fwd(const FwdParams& p) {
     case kFwdD128CausalPair4: return launch_fwd_dl<128, 64, 4, 2, true>(p);
     default: return launch_fwd_dl<128, 64, 8, 2, true>(p);
   }
-}
-
-int split_kv_slices(int B, int H, int N, int requested) {
-  if (requested > 0) return requested;
-  // enough work items for two 4-wave workgroups per CU, at most 16 slices,
-  // and at least two 64-key tiles per slice
-  constexpr long long kCus = 256;
-  const long long items = (long long)B * H * ((N + 127) / 128);
-  long long s = (2 * kCus + items - 1) / items;
-  const long long max_by_keys = ((N + 63) / 64) / 2;
-  s = s < 16 ? s : 16;
-  s = s < max_by_keys ? s : max_by_keys;
-  return (int)(s < 1 ? 1 : s);
 }
 
 hipError_t launch_fwd_split_kv(const FwdParams& p) {

@@ -22,7 +22,8 @@
  *    (element (b, n, h, c) at ((b*N + n)*H + h)*d + c).
  *  - L (lse): float32, [B, H, N] contiguous; natural-log logsumexp of the
  *    scaled, masked scores of each query row.
- *  - d must be 64 or 128.  B, H, N >= 0; B*H*N == 0 is a successful no-op.
+ *  - d must be 64 or 128.  B, H, N >= 0, N <= 2^30; B*H*N == 0 is a
+ *    successful no-op.
  *  - scale: any finite float with |scale| * log2(e) finite in fp32, i.e.
  *    |scale| <= 2.35e38 (usually 1/sqrt(d)).
  *  - Every pointer is a DEVICE pointer owned by the caller; the library keeps
@@ -48,8 +49,8 @@ extern "C" {
 typedef enum fa2_status {
   FA2_OK = 0,
   FA2_ERR_NULLPTR = 1,   /* a required pointer is NULL and the problem is non-empty */
-  FA2_ERR_SHAPE = 2,     /* B, H or N negative, B*H*N exceeds 2^31 - 1, or H*d    */
-                         /* (elements of one token) exceeds 2^23                  */
+  FA2_ERR_SHAPE = 2,     /* B, H or N negative, N above 2^30, B*H*N above         */
+                         /* 2^31 - 1, or H*d (elements of one token) above 2^23   */
   FA2_ERR_HEADDIM = 3,   /* d is not 64 or 128                                    */
   FA2_ERR_SCALE = 4,     /* scale is NaN or infinite, or |scale| > 2.35e38        */
   FA2_ERR_ALIGN = 5,     /* a base pointer is not 16-byte (lse: 4-byte) aligned   */

@@ -82,6 +82,11 @@ def test_fwd_argument_errors(L):
     assert fwd(L, lse=LSE + 2) == ALIGN
     # grid would exceed the launch limit
     assert fwd(L, B=1 << 20, H=1 << 10, N=1 << 20) == SHAPE
+    # N above 2^30 (token indices plus a tile must stay inside int); at
+    # exactly 2^30 the shape passes and the NULL q is what fails
+    assert fwd(L, B=1, H=1, N=(1 << 30) + 1) == SHAPE
+    assert fwd(L, B=1, H=1, N=2147483647) == SHAPE
+    assert fwd(L, q=None, B=1, H=1, N=1 << 30) == NULLPTR
     # one token wider than 2^23 elements: in-tile row offsets would leave 32
     # bits.  At exactly 2^23 the shape passes and the NULL q is what fails.
     assert fwd(L, B=1, H=(1 << 16) + 1, N=8, d=128) == SHAPE
