@@ -144,23 +144,27 @@ def calibrate_copy(mib: int) -> None:
                       "ms": round(ms, 4), "GB_per_s": round(2 * n / ms / 1e6, 1)}), flush=True)
 
 
-def measured_mfma_peak(stream, blocks: int = 2048, iters: int = 4000) -> float:
+def measured_mfma_peak(stream, random_operands: bool = False, blocks: int = 2048,
+                       iters: int = 4000) -> float:
     """bf16 MFMA TFLOP/s of the library's calibration kernel (two waves per
     SIMD issuing back-to-back MFMAs from registers), best of three timed
-    calls after one warm-up: the attainable peak at the running clock."""
+    calls after one warm-up: the attainable peak at the running clock.  With
+    random_operands the operands change from one MFMA to the next as in an
+    attention tile, which draws more power and so runs at a lower clock."""
     import torch
 
     from exact_tiled_attention_30_amd import binding
 
+    fn = binding.fa2_calibrate_mfma_random if random_operands else binding.fa2_calibrate_mfma
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-    binding.fa2_calibrate_mfma(out, blocks, iters, stream.cuda_stream)
+    fn(out, blocks, iters, stream.cuda_stream)
     flops = blocks * 4 * iters * 4 * 32768.0
     best = float("inf")
     for _ in range(3):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        binding.fa2_calibrate_mfma(out, blocks, iters, stream.cuda_stream)
+        fn(out, blocks, iters, stream.cuda_stream)
         b.record(stream)
         b.synchronize()
         best = min(best, a.elapsed_time(b))
@@ -346,6 +350,7 @@ def main():
     achieved = dom_flops / (per_kernel_ms[dom] * 1e-3) / 1e12
 
     peak_clock = measured_mfma_peak(stream)
+    peak_random = measured_mfma_peak(stream, random_operands=True)
 
     roofline = {
         "bound": "mfma",
@@ -358,9 +363,13 @@ def main():
         "avg_launch_ms": round(per_kernel_ms[dom], 5),
         "flops_per_launch": dom_flops,
         # the same kernel against what plain back-to-back MFMAs reach at the
-        # clock the GPU runs at (fa2_calibrate_mfma, timed right after)
+        # clock the GPU runs at (fa2_calibrate_mfma, timed right after) ...
         "peak_measured": round(peak_clock, 1),
         "frac_of_measured": round(achieved / peak_clock, 4),
+        # ... and when their operands change like an attention tile's
+        # (fa2_calibrate_mfma_random): the power cap then lowers the clock
+        "peak_measured_random": round(peak_random, 1),
+        "frac_of_measured_random": round(achieved / peak_random, 4),
     }
 
     if args.no_cpu:

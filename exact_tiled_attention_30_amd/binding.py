@@ -8,7 +8,8 @@ library is missing the call fails loudly.
 Names mirror include/fa2.h: fa2_fwd, fa2_bwd, fa2_bwd_workspace_bytes, fa2_bwd_noalloc,
 fa2_bwd_atomic_dq, fa2_bwd_atomic_dq_workspace_bytes, fa2_fwd_split_kv,
 fa2_fwd_split_kv_workspace_bytes, fa2_fwd_fa1_order, fa2_fwd_fa1_order_workspace_bytes,
-fa2_fwd_variant, fa2_bwd_variant, fa2_variant_name, fa2_calibrate_mfma, fa2_status_string.
+fa2_fwd_variant, fa2_bwd_variant, fa2_variant_name, fa2_calibrate_mfma,
+fa2_calibrate_mfma_random, fa2_status_string.
 """
 from __future__ import annotations
 
@@ -69,6 +70,8 @@ def lib():
     L.fa2_fwd_fa1_order.restype = _i
     L.fa2_calibrate_mfma.argtypes = [_vp, _i, _i, _vp]
     L.fa2_calibrate_mfma.restype = _i
+    L.fa2_calibrate_mfma_random.argtypes = [_vp, _i, _i, _vp]
+    L.fa2_calibrate_mfma_random.restype = _i
     L.fa2_fwd_variant.argtypes = [_i, _i, _i, _i, _i, _i]
     L.fa2_fwd_variant.restype = _i
     L.fa2_bwd_variant.argtypes = [_i, _i, _i, _i, _i]
@@ -104,12 +107,24 @@ def fa2_calibrate_mfma(out, blocks: int, iters: int, stream=None) -> None:
     """Measurement helper: `blocks` x 256 threads of back-to-back bf16 MFMAs
     (blocks x 4 x iters x 4 x 32768 FLOP); `out` a float32 device tensor of
     at least blocks x 256 elements.  Time it with events on `stream`."""
+    _calibrate(lib().fa2_calibrate_mfma, out, blocks, iters, stream)
+
+
+def fa2_calibrate_mfma_random(out, blocks: int, iters: int, stream=None) -> None:
+    """As fa2_calibrate_mfma, with changing unit-variance random operands:
+    the MFMA rate a power-capped GPU sustains on real data."""
+    _calibrate(lib().fa2_calibrate_mfma_random, out, blocks, iters, stream)
+
+
+def _calibrate(fn, out, blocks: int, iters: int, stream) -> None:
     import torch
 
-    _require(out, torch.float32, "out")
+    if out.dtype != torch.float32:
+        raise TypeError(f"out must be {torch.float32}, got {out.dtype}")
     if out.numel() < blocks * 256:
         raise ValueError("out is too small")
-    _check(lib().fa2_calibrate_mfma(_ptr(out), int(blocks), int(iters), _stream(out, stream)))
+    _require(out, torch.float32, "out")
+    _check(fn(_ptr(out), int(blocks), int(iters), _stream(out, stream)))
 
 
 def _check(status: int) -> None:

@@ -262,6 +262,15 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
+int calibrate(float* out, int blocks, int iters, bool random_operands, void* stream) {
+  if (out == nullptr) return FA2_ERR_NULLPTR;
+  if (blocks < 1 || iters < 1) return FA2_ERR_SHAPE;
+  return fa2::launch_calib_mfma(out, blocks, iters, random_operands, (hipStream_t)stream) ==
+                 hipSuccess
+             ? FA2_OK
+             : FA2_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -294,11 +303,11 @@ const char* fa2_variant_name(int variant) {
 }
 
 int fa2_calibrate_mfma(float* out, int blocks, int iters, void* stream) {
-  if (out == nullptr) return FA2_ERR_NULLPTR;
-  if (blocks < 1 || iters < 1) return FA2_ERR_SHAPE;
-  return fa2::launch_calib_mfma(out, blocks, iters, (hipStream_t)stream) == hipSuccess
-             ? FA2_OK
-             : FA2_ERR_LAUNCH;
+  return calibrate(out, blocks, iters, false, stream);
+}
+
+int fa2_calibrate_mfma_random(float* out, int blocks, int iters, void* stream) {
+  return calibrate(out, blocks, iters, true, stream);
 }
 
 int fa2_bwd_atomic_dq(const void* q, const void* k, const void* v, const void* o,

@@ -9,8 +9,9 @@
 namespace fa2 {
 
 // Kernel configuration of the forward pass for a problem.  Tile shapes (K/V
-// tile 64 keys; 8 waves = 256-row Q tiles, or 4 waves = 128 rows) chosen by
-// measurement on MI355X, each parity-tested.  Grids of fewer 8-wave Q tiles
+// tile 64 keys, 128 for the 8-wave causal d = 128 pairs; 8 waves = 256-row Q
+// tiles, or 4 waves = 128 rows) chosen by measurement on MI355X, each
+// parity-tested.  Grids of fewer 8-wave Q tiles
 // than CUs use 4-wave tiles (twice the workgroups); causal grids of fewer
 // than two 8-wave workgroups per CU use the 4-wave tiles too, and grids of
 // fewer 4-wave pairs than CUs drop the pairing.  Causal grids with whole
@@ -64,7 +65,7 @@ const char* fwd_variant_name(int v) {
     case kFwdD128CausalDealt: return "fwd_dl_kernel<128,64,4,2,true,false,false,true>";
     case kFwdD128CausalOne: return "fwd_dl_kernel<128,64,4,2,true,false,false>";
     case kFwdD128CausalPair4: return "fwd_dl_kernel<128,64,4,2,true>";
-    case kFwdD128CausalPair8: return "fwd_dl_kernel<128,64,8,2,true>";
+    case kFwdD128CausalPair8: return "fwd_dl_kernel<128,128,8,2,true>";
     default: return nullptr;
   }
 }

@@ -784,7 +784,7 @@ hipError_t launch_fwd(const FwdParams& p) {
     case kFwdD128CausalDealt: return launch_fwd_dl<128, 64, 4, 2, true, false, true>(p);
     case kFwdD128CausalOne: return launch_fwd_dl<128, 64, 4, 2, true, false>(p);
     case kFwdD128CausalPair4: return launch_fwd_dl<128, 64, 4, 2, true>(p);
-    default: return launch_fwd_dl<128, 64, 8, 2, true>(p);
+    default: return launch_fwd_dl<128, 128, 8, 2, true>(p);
   }
 }
 

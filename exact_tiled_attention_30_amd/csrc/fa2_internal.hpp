@@ -118,6 +118,7 @@ int split_kv_slices(int B, int H, int N, int requested);
 hipError_t launch_fa1_order_fwd(const Fa1Params& p);
 hipError_t launch_bwd(const BwdParams& p);             // dQ from a Q-outer pass
 hipError_t launch_bwd_atomic_dq(const BwdParams& p);   // dQ summed with fp32 atomics
-hipError_t launch_calib_mfma(float* out, int blocks, int iters, hipStream_t stream);
+hipError_t launch_calib_mfma(float* out, int blocks, int iters, bool random_operands,
+                             hipStream_t stream);
 
 }  // namespace fa2

@@ -221,6 +221,17 @@ int fa2_fwd_fa1_order(const void* q, const void* k, const void* v, void* o, floa
  */
 int fa2_calibrate_mfma(float* out, int blocks, int iters, void* stream);
 
+/* Measurement helper, not part of the attention path: as fa2_calibrate_mfma
+ * (same grid, same FLOPs per call, same `out` contract and errors), but each
+ * wave cycles through 8 operand pairs of unit-variance pseudo-random bf16
+ * values, a different pair for every MFMA of a chain, as the operands of an
+ * attention tile change from one MFMA to the next.  The matrix cores draw
+ * more power when more operand bits toggle, so on a power-capped GPU this
+ * mode settles at a lower clock than the fixed-operand one: its throughput is
+ * the bf16 MFMA rate attainable on real data.
+ */
+int fa2_calibrate_mfma_random(float* out, int blocks, int iters, void* stream);
+
 /*
  * Diagnostics, not part of the attention path: which kernel configuration
  * (tile shape, waves per workgroup, causal work assignment) fa2_fwd and

@@ -23,7 +23,7 @@ hipError_t launch_fwd_split_kv(const FwdParams&) { return never("split_kv"); }
 hipError_t launch_fa1_order_fwd(const Fa1Params&) { return never("fa1_order"); }
 hipError_t launch_bwd(const BwdParams&) { return never("bwd"); }
 hipError_t launch_bwd_atomic_dq(const BwdParams&) { return never("bwd_atomic"); }
-hipError_t launch_calib_mfma(float*, int, int, hipStream_t) { return never("calib"); }
+hipError_t launch_calib_mfma(float*, int, int, bool, hipStream_t) { return never("calib"); }
 int fwd_resident_d128() { return 2; }
 }  // namespace fa2
 
@@ -98,6 +98,8 @@ int main() {
   expect(fa2_fwd_fa1_order(P[0], P[1], P[2], P[3], L, nullptr, 0, 2, 3, 100, 64, 0, 0.1f, 1,
                            nullptr), FA2_ERR_WORKSPACE, "fa1 without workspace");
   expect(fa2_calibrate_mfma(nullptr, 1, 1, nullptr), FA2_ERR_NULLPTR, "calib null");
+  expect(fa2_calibrate_mfma_random((float*)P[9], 0, 1, nullptr), FA2_ERR_SHAPE,
+         "calib random blocks");
   // the dispatch over a range of valid shapes: every id names a kernel
   for (int B : {1, 2, 3, 8, 80})
     for (int H : {1, 2, 9, 16, 64})

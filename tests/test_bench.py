@@ -109,6 +109,9 @@ def test_bench_json_line():
     rf = d["roofline"]
     assert rf["bound"] == "mfma" and rf["peak"] == 2516.6 and rf["unit"] == "TFLOP/s"
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    # both calibration modes ran; changing operands never beat the data sheet
+    assert 0 < rf["peak_measured_random"] <= rf["peak"] and 0 < rf["peak_measured"] <= rf["peak"]
+    assert abs(rf["frac_of_measured_random"] - rf["achieved"] / rf["peak_measured_random"]) < 1e-3
     # HBM bytes from the committed counter runs, or null once the kernels changed
     assert rf["traffic"] is None or rf["traffic"] > 0
     cb = d["cpu_baseline"]

@@ -69,5 +69,8 @@ def test_backward_rejects_bad_tensors():
 
 
 def test_calibration_rejects_bad_output():
-    with pytest.raises(TypeError):
-        binding.fa2_calibrate_mfma(torch.zeros(256, dtype=torch.float64), 1, 1)
+    for fn in (binding.fa2_calibrate_mfma, binding.fa2_calibrate_mfma_random):
+        with pytest.raises(TypeError):
+            fn(torch.zeros(256, dtype=torch.float64), 1, 1)
+        with pytest.raises(ValueError, match="too small"):
+            fn(torch.zeros(255, dtype=torch.float32), 1, 1)

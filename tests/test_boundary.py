@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == ["fa2_bwd", "fa2_bwd_atomic_dq",
                                     "fa2_bwd_atomic_dq_workspace_bytes", "fa2_bwd_noalloc",
                                     "fa2_bwd_variant", "fa2_bwd_workspace_bytes",
-                                    "fa2_calibrate_mfma", "fa2_fwd", "fa2_fwd_fa1_order",
+                                    "fa2_calibrate_mfma", "fa2_calibrate_mfma_random",
+                                    "fa2_fwd", "fa2_fwd_fa1_order",
                                     "fa2_fwd_fa1_order_workspace_bytes", "fa2_fwd_split_kv",
                                     "fa2_fwd_split_kv_workspace_bytes", "fa2_fwd_variant",
                                     "fa2_status_string", "fa2_variant_name"]
@@ -239,7 +240,8 @@ def test_split_kv_argument_errors(L):
 def test_calibrate_mfma_argument_errors(L):
     # host-side validation only (no launch): a NULL buffer or a non-positive
     # size is rejected before any HIP call
-    assert L.fa2_calibrate_mfma(None, 1, 1, None) == 1          # FA2_ERR_NULLPTR
     fake = ctypes.c_void_p(256)
-    assert L.fa2_calibrate_mfma(fake, 0, 1, None) == 2          # FA2_ERR_SHAPE
-    assert L.fa2_calibrate_mfma(fake, 1, 0, None) == 2
+    for fn in (L.fa2_calibrate_mfma, L.fa2_calibrate_mfma_random):
+        assert fn(None, 1, 1, None) == 1          # FA2_ERR_NULLPTR
+        assert fn(fake, 0, 1, None) == 2          # FA2_ERR_SHAPE
+        assert fn(fake, 1, 0, None) == 2

@@ -41,7 +41,7 @@ def test_variant_ids_and_names():
     assert binding.fa2_bwd_variant(-1, 1, 128, 64, True) == -1
     # the documented picks of the measured workloads
     assert binding.fa2_variant_name(binding.fa2_fwd_variant(1, 16, 32768, 128, True, 2)) == \
-        "fwd_dl_kernel<128,64,8,2,true>"
+        "fwd_dl_kernel<128,128,8,2,true>"
     assert binding.fa2_variant_name(binding.fa2_fwd_variant(4, 16, 4096, 128, False)) == \
         "fwd_sp_kernel<128,64,8>"
     assert binding.fa2_variant_name(binding.fa2_bwd_variant(4, 16, 4096, 128, True)) == \

@@ -286,9 +286,12 @@ def test_full_size_workloads(w):
 
 # Causal shapes whose B*H is not a multiple of 8 reach the paired work
 # assignments of the forward dispatch (4-wave pairs at d = 64 and 128, 8-wave
-# pairs at d = 64) that the workloads above do not: every element of the
-# first and last head, and >= 4096 rows over all heads.
-DISPATCH_SHAPES = [(1, 9, 8192, 64), (1, 25, 16384, 64), (1, 9, 8192, 128)]
+# pairs at d = 64) that the workloads above do not; the last two are 8-wave
+# d = 128 pairs (128-key K/V tiles) over short sequences: one partial tile
+# (N = 100), and two full tiles and a partial one (N = 300).  Every element of
+# the first and last head, and >= 4096 rows over all heads.
+DISPATCH_SHAPES = [(1, 9, 8192, 64), (1, 25, 16384, 64), (1, 9, 8192, 128),
+                   (2, 515, 100, 128), (1, 1030, 300, 128)]
 
 
 @pytest.mark.parametrize("shape", DISPATCH_SHAPES, ids=lambda s: "b{}h{}n{}d{}".format(*s))
