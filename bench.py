@@ -116,6 +116,11 @@ def parse_args():
                    help="forward workloads: alternate between two resident input sets "
                         "(and two outputs), so consecutive calls do not find their "
                         "inputs in the 256 MiB last-level cache when a set is larger")
+    p.add_argument("--zero-inputs", action="store_true",
+                   help="diagnostic: every input tensor zero (no oracle baseline, no parity). "
+                        "The kernels execute the same instructions on any data, but the GPU's "
+                        "clock under its power cap depends on how many operand bits toggle; "
+                        "compared with the default run this shows that dependence")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (for scaling the "
                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -250,6 +255,9 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     host = inputs_for(base)
+    if args.zero_inputs:
+        host = {n: torch.zeros_like(t) for n, t in host.items()}
+        args.no_cpu = True
     x = {n: t.to(dev) for n, t in host.items()}
     o = torch.empty_like(x["q"])
     lse = torch.empty((base.B, base.H, base.N), dtype=torch.float32, device=dev)
@@ -392,7 +400,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "zeros (clock diagnostic)" if args.zero_inputs else "synthetic",
         "config": {
             "workload": "+".join(w.name for w in ws),
             "B": base.B, "H": base.H, "N": base.N, "d": base.d,
