@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void calib_mfma_kernel(float* __restrict__ out
 #pragma unroll
   for (int c = 0; c < kCalibChains; ++c) acc[c] = f32x16{};
   int it = 0;
-  for (; it + kSets <= iters; it += kSets) {
+  for (; it <= iters - kSets; it += kSets) {  // iters >= 1: no overflow
 #pragma unroll
     for (int s = 0; s < kSets; ++s)
 #pragma unroll
