@@ -713,17 +713,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
       if (jt + 1 < n_kv) step(jt + 1, kb1, vb1, kb0, vb0);
     }
 
-    if (my_q < N) {
-      uint16_t* op = dq + head + (size_t)my_q * tok;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 x = f32x4{dqa[dt][4 * g + 0], dqa[dt][4 * g + 1], dqa[dt][4 * g + 2],
-                                dqa[dt][4 * g + 3]} * scale;
-          *(u32x2*)(op + dt * 32 + 8 * g + 4 * hi) = __builtin_bit_cast(u32x2, to_bf16x4(x));
-        }
-    }
+    store_row_bf16<D>(dq + head + (size_t)qc * tok, dqa, scale, hi, my_q < N);
   }
 }
 

@@ -102,6 +102,43 @@ __device__ __forceinline__ bool wave_any(bool p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// One output row in bf16, scaled by `mul`, from transposed accumulators
+// (acc[dt] = 32 columns x 32 rows, the row fixed per lane), stored 16 bytes
+// per lane.  Accumulator register 4g + i of lane (row, half h) is column
+// dt*32 + 8g + 4h + i: 8-byte pieces that alternate between the row's two
+// lanes.  One v_permlane32_swap per register pair trades the lower lane's
+// piece g = 2j+1 for the upper lane's piece g = 2j, so each lane holds the 8
+// consecutive columns dt*32 + 16j + 8h .. +7 and every store instruction
+// writes 32 contiguous bytes per row instead of 16: half the instructions and
+// half the memory requests of an epilogue that every workgroup of a short
+// launch runs at once.  All lanes must call it (the swap reads the partner
+// lane); `valid` gates the store, `dst` points at the row's first column.
+template <int D>
+__device__ __forceinline__ void store_row_bf16(uint16_t* dst, const f32x16 (&acc)[D / 32], float mul,
+                                               int hi, bool valid) {
+  u32x4 row[D / 32][2];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x16& a = acc[dt];
+      const u32x2 even = __builtin_bit_cast(
+          u32x2, to_bf16x4(f32x4{a[8 * j], a[8 * j + 1], a[8 * j + 2], a[8 * j + 3]} * mul));
+      const u32x2 odd = __builtin_bit_cast(
+          u32x2, to_bf16x4(f32x4{a[8 * j + 4], a[8 * j + 5], a[8 * j + 6], a[8 * j + 7]} * mul));
+      // lower lane: (own even, partner's even); upper lane: (partner's odd, own odd)
+      const auto w0 = __builtin_amdgcn_permlane32_swap(even[0], odd[0], false, false);
+      const auto w1 = __builtin_amdgcn_permlane32_swap(even[1], odd[1], false, false);
+      row[dt][j] = u32x4{w0[0], w1[0], w0[1], w1[1]};
+    }
+  if (valid) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) *(u32x4*)(dst + dt * 32 + 16 * j + 8 * hi) = row[dt][j];
+  }
+}
+
 // s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt in
 // bits 6:4, lgkmcnt in bits 11:8).  Before a barrier after which another
 // wave's global_load_lds may overwrite an LDS buffer, a wave must have both

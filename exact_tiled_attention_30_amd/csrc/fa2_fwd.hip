@@ -60,42 +60,6 @@ __device__ __forceinline__ float next_threshold(float m_run, float l_lane) {
                                          kMaxSlack);
 }
 
-// O row of this lane's query, normalised and rounded to bf16, stored 16 bytes
-// per lane.  The O^T accumulators give lane (q, half h) the columns
-// dt*32 + 8g + 4h .. +3 of its row, g = 0..3: 8-byte pieces, which alternate
-// between the two lanes of the row.  One v_permlane32_swap per register pair
-// trades the lower lane's piece g = 2j+1 for the upper lane's piece g = 2j, so
-// that each lane holds 8 consecutive columns, dt*32 + 16j + 8h .. +7, and every
-// store instruction writes 32 contiguous bytes per row instead of 16: half the
-// store instructions and half the memory requests of the epilogue, which runs
-// on every workgroup at once at the end of a short launch.  All lanes must
-// call it (the swap reads the partner lane); `valid` gates the store.
-template <int D>
-__device__ __forceinline__ void store_o_row(uint16_t* op, const f32x16 (&oacc)[D / 32], float inv,
-                                            int hi, bool valid) {
-  u32x4 row[D / 32][2];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const f32x16& a = oacc[dt];
-      const u32x2 even = __builtin_bit_cast(
-          u32x2, to_bf16x4(f32x4{a[8 * j], a[8 * j + 1], a[8 * j + 2], a[8 * j + 3]} * inv));
-      const u32x2 odd = __builtin_bit_cast(
-          u32x2, to_bf16x4(f32x4{a[8 * j + 4], a[8 * j + 5], a[8 * j + 6], a[8 * j + 7]} * inv));
-      // lower lane: (own even, partner's even); upper lane: (partner's odd, own odd)
-      const auto w0 = __builtin_amdgcn_permlane32_swap(even[0], odd[0], false, false);
-      const auto w1 = __builtin_amdgcn_permlane32_swap(even[1], odd[1], false, false);
-      row[dt][j] = u32x4{w0[0], w1[0], w0[1], w1[1]};
-    }
-  if (valid) {
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) *(u32x4*)(op + dt * 32 + 16 * j + 8 * hi) = row[dt][j];
-  }
-}
-
 // ---------------------------------------------------------------------------
 // K and V tiles move HBM/L2 -> LDS with global_load_lds_dwordx4: lane L of a
 // wave deposits its 16 bytes at LDS base + 16*L, so no VGPRs, no ds_write and
@@ -397,7 +361,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W * 
             l > 0.f ? m_run + log2f(l) : -INFINITY;
     }
   } else {
-  store_o_row<D>(o + head + (size_t)min(my_q, N - 1) * tok, oacc, 1.0f / l, hi, my_q < N);
+  store_row_bf16<D>(o + head + (size_t)min(my_q, N - 1) * tok, oacc, 1.0f / l, hi, my_q < N);
   if (my_q < N && hi == 0) lse[((size_t)b * H + hh) * N + my_q] = (m_run + log2f(l)) * kLn2;
   }
   if (pass + 1 < n_pass) {
@@ -702,7 +666,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(8 / W)))
   }
 
   const float l = pair_sum(l_part);
-  store_o_row<D>(o + head + (size_t)min(my_q, N - 1) * tok, oacc, 1.0f / l, hi, my_q < N);
+  store_row_bf16<D>(o + head + (size_t)min(my_q, N - 1) * tok, oacc, 1.0f / l, hi, my_q < N);
   if (my_q < N && hi == 0) lse[((size_t)b * H + hh) * N + my_q] = (m_run + log2f(l)) * kLn2;
 }
 
