@@ -923,7 +923,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
           }
         }
 
-        // dV += P^T dO and dK += dS^T Q over the wave's 32 queries; the
+        // dV^T += dO^T P and dK^T += Q^T dS over the wave's 32 queries: the
+        // same fragments as dV = P^T dO with the operands swapped (the
+        // 32x32x16 MFMA's A rows and B columns take the same lane layout),
+        // so the key stays on the lane and d runs down the registers; the
         // transposed dO / Q fragments run one product pair ahead
         bf16x8 pf[2], dsf[2];
 #pragma unroll
@@ -946,8 +949,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
         for (int i = 0; i < kPairs; ++i) {
           const int c2 = i / DT, dt = i % DT;
-          dv_acc[dt] = mfma32(pf[c2], ofr[i % 2], dv_acc[dt]);
-          dk_acc[dt] = mfma32(dsf[c2], qfr[i % 2], dk_acc[dt]);
+          dv_acc[dt] = mfma32(ofr[i % 2], pf[c2], dv_acc[dt]);
+          dk_acc[dt] = mfma32(qfr[i % 2], dsf[c2], dk_acc[dt]);
           if (i + 2 < kPairs) tload(i + 2, i % 2);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -962,23 +965,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
 
     // The two waves of a key block add their partials through LDS (the Q/dO
     // buffers are free now): the upper half stores, the lower half adds and
-    // writes out.  Layout [register][lane] keeps the accesses conflict-free.
+    // writes out.  The accumulators hold dK^T and dV^T (the key on the lane,
+    // d in the registers, as O^T in the forward pass), so a partial moves as
+    // 16-byte chunks in [chunk][lane] order (conflict-free), and the sum
+    // leaves through store_row_bf16: 16 bytes of a key's row per lane.
     uint8_t* const red = kb == 0 ? q_s0 : kb == 1 ? q_s1 : kb == 2 ? do_s0 : do_s1;
     auto put = [&](const f32x16* acc) __attribute__((always_inline)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ((float*)red)[(dt * 16 + r) * 64 + lane] = acc[dt][r];
+        for (int g = 0; g < 4; ++g)
+          ((f32x4*)red)[(dt * 4 + g) * 64 + lane] =
+              f32x4{acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]};
     };
-    auto add_store = [&](const f32x16* acc, uint16_t* dst, float mul) __attribute__((always_inline)) {
+    auto add_store = [&](f32x16* acc, uint16_t* dst, float mul) __attribute__((always_inline)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = acc[dt][r] + ((const float*)red)[(dt * 16 + r) * 64 + lane];
-          const int key = kw0 + acc_row(r, hi);
-          if (key < N) dst[head + (size_t)key * tok + dt * 32 + l32] = to_bf16_bits(mul * x);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 other = ((const f32x4*)red)[(dt * 4 + g) * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[dt][4 * g + i] += other[i];
         }
+      store_row_bf16<D>(dst + head + (size_t)min(my_key, N - 1) * tok, acc, mul, hi, my_key < N);
     };
     if (qh == 1) put(dk_acc);
     wait_dma_and_lds();

@@ -103,7 +103,7 @@ __device__ __forceinline__ bool wave_any(bool p) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // One output row in bf16, scaled by `mul`, from transposed accumulators
-// (acc[dt] = 32 columns x 32 rows, the row fixed per lane), stored 16 bytes
+// (acc[dt], dt < D / 32: 32 columns x 32 rows, the row fixed per lane), stored 16 bytes
 // per lane.  Accumulator register 4g + i of lane (row, half h) is column
 // dt*32 + 8g + 4h + i: 8-byte pieces that alternate between the row's two
 // lanes.  One v_permlane32_swap per register pair trades the lower lane's
@@ -114,7 +114,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // launch runs at once.  All lanes must call it (the swap reads the partner
 // lane); `valid` gates the store, `dst` points at the row's first column.
 template <int D>
-__device__ __forceinline__ void store_row_bf16(uint16_t* dst, const f32x16 (&acc)[D / 32], float mul,
+__device__ __forceinline__ void store_row_bf16(uint16_t* dst, const f32x16* acc, float mul,
                                                int hi, bool valid) {
   u32x4 row[D / 32][2];
 #pragma unroll
