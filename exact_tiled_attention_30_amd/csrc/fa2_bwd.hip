@@ -23,9 +23,11 @@
 //   * it walks 64-query steps of Q, dO and the L / D rows, moved global ->
 //     LDS by DMA one step ahead into a second buffer;
 //   * S = K Q^T and dP = V dO^T put the key on the lane, so P and dS feed the
-//     dV += P dO and dK += dS Q products straight from registers (as A
-//     operands), with dO^T and Q^T read transposed from the same row-major
-//     LDS tiles; with the atomic dQ strategy, dS also goes to LDS, from which
+//     dV^T += dO^T P and dK^T += Q^T dS products straight from registers (as
+//     B operands), with dO^T and Q^T read transposed from the same row-major
+//     LDS tiles; the transposed accumulators keep the key on the lane, so the
+//     dK and dV rows leave 16 bytes per lane; with the atomic dQ strategy,
+//     dS also goes to LDS, from which
 //     the workgroup forms its dQ partial = dS K over its 128 keys and adds it
 //     atomically.
 // For d = 128 the two-pass path runs bwd_kv_pair_kernel instead: the same
@@ -431,8 +433,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
                                            dp[r0 + 4], dp[r0 + 5], dp[r0 + 6], dp[r0 + 7]});
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          dv_acc[dt] = mfma32(pf, tr_frag<RB>(dos, trq, dt, 2 * t + c2), dv_acc[dt]);
-          dk_acc[dt] = mfma32(dsf, tr_frag<RB>(qs, trq, dt, 2 * t + c2), dk_acc[dt]);
+          // dV^T += dO^T P, dK^T += Q^T dS: the key on the lane, d down the
+          // registers, so the rows leave 16 bytes per lane (store_row_bf16)
+          dv_acc[dt] = mfma32(tr_frag<RB>(dos, trq, dt, 2 * t + c2), pf, dv_acc[dt]);
+          dk_acc[dt] = mfma32(tr_frag<RB>(qs, trq, dt, 2 * t + c2), dsf, dk_acc[dt]);
         }
       }
       interleave_lds_mfma<2 * 2 * (D / 32), 2, 3>();
@@ -480,17 +484,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
   }
   if constexpr (ATOMIC_DQ) if (q0_pend >= 0) flush_dq();
 
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kw0 + acc_row(r, hi);
-      if (key < N) {
-        const size_t off = head + (size_t)key * tok + dt * 32 + l32;
-        dk[off] = to_bf16_bits(scale * dk_acc[dt][r]);
-        dv[off] = to_bf16_bits(dv_acc[dt][r]);
-      }
-    }
+  store_row_bf16<D>(dk + head + (size_t)min(my_key, N - 1) * tok, dk_acc, scale, hi, my_key < N);
+  store_row_bf16<D>(dv + head + (size_t)min(my_key, N - 1) * tok, dv_acc, 1.0f, hi, my_key < N);
   }
 }
 
