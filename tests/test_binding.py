@@ -74,3 +74,15 @@ def test_calibration_rejects_bad_output():
             fn(torch.zeros(256, dtype=torch.float64), 1, 1)
         with pytest.raises(ValueError, match="too small"):
             fn(torch.zeros(255, dtype=torch.float32), 1, 1)
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    # no libfa2.so: loading it raises, there is no other implementation to fall back to
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libfa2.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="is not built"):
+        binding.lib()
+    # and host tensors are rejected by the checks, never computed on the CPU
+    q, k, v, _, _ = fwd_args()
+    with pytest.raises(ValueError, match="device tensor"):
+        binding.attention_forward(q, k, v, causal=True)
