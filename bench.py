@@ -57,7 +57,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 KERNEL_SOURCES = {
-    False: ("fa2_device.hpp", "fa2_internal.hpp", "fa2_fwd.hip"),
+    False: ("fa2_device.hpp", "fa2_internal.hpp", "fa2_fwd_kernels.hpp", "fa2_fwd.hip",
+            "fa2_fwd_wide.hip"),
     True: ("fa2_device.hpp", "fa2_internal.hpp", "fa2_bwd.hip"),
 }
 

@@ -26,7 +26,7 @@ HIP_SOURCES = [s for s in build.SOURCES if s.endswith(".hip")]
 
 def _asm(src, out_dir):
     out = os.path.join(out_dir, os.path.basename(src) + ".s")
-    cmd = [build.hipcc(), *[f for f in build.HIPCC_FLAGS if f not in ("-shared", "-fPIC")],
+    cmd = [build.hipcc(), *[f for f in build.compile_flags(src) if f != "-fPIC"],
            "--cuda-device-only", "-S", "-I", build.INCLUDE, "-I", build.CSRC,
            os.path.join(build.CSRC, src), "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
