@@ -984,17 +984,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void b
         }
       store_row_bf16<D>(dst + head + (size_t)min(my_key, N - 1) * tok, acc, mul, hi, my_key < N);
     };
+    // No DMA is in flight here (the last step issued none), so the barriers
+    // wait for LDS accesses only and the dK/dV stores drain in the background.
     if (qh == 1) put(dk_acc);
-    wait_dma_and_lds();
+    wait_lds();
     __syncthreads();
     if (qh == 0) add_store(dk_acc, dk, scale);
-    wait_dma_and_lds();
+    wait_lds();
     __syncthreads();
     if (qh == 1) put(dv_acc);
-    wait_dma_and_lds();
+    wait_lds();
     __syncthreads();
     if (qh == 0) add_store(dv_acc, dv, 1.0f);
-    wait_dma_and_lds();
+    wait_lds();
     __syncthreads();
   }
 }
