@@ -187,6 +187,12 @@ __device__ __forceinline__ void interleave_lds_mfma() {
 
 // Hides a value from loop-invariant code motion, so addresses derived from
 // it are formed where they are used instead of being hoisted and held live.
+// lgkmcnt(0) alone (vmcnt and expcnt at their maximum; gfx9 s_waitcnt
+// layout): before a barrier at which no DMA is outstanding, so global stores
+// still in flight need not drain first.
+constexpr int kWaitLgkm = 0xC07F;
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(kWaitLgkm); }
+
 __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;

@@ -148,11 +148,6 @@ __device__ __forceinline__ void store_row_bf16(uint16_t* dst, const f32x16* acc,
 // compiler may schedule a read's consumer after the barrier.
 constexpr int kWaitVmLgkm = 0x0070;  // vmcnt(0) lgkmcnt(0)
 __device__ __forceinline__ void wait_dma_and_lds() { __builtin_amdgcn_s_waitcnt(kWaitVmLgkm); }
-// lgkmcnt(0) alone (vmcnt and expcnt at their maximum): before a barrier at
-// which no DMA is outstanding, so global stores still in flight need not
-// drain first.
-constexpr int kWaitLgkm = 0xC07F;
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(kWaitLgkm); }
 
 // Workgroups are dispatched round-robin over the eight XCDs (wg i runs on XCD
 // i % 8).  Renumber them so that each XCD receives one contiguous range of
